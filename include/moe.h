@@ -1,0 +1,190 @@
+/*
+ * moe.h — C interface of the MI355X (gfx950) sparse mixture-of-experts
+ * feed-forward layer, forward pass.
+ *
+ * The layer (from the "gpt-oss-40b-64a8-init" LLM-surgery page, section 2
+ * "Mathematical Foundation: Silent Init", Proof; and the "gpt-oss 20B" field
+ * guide, cutaway 03 "Sparse Mixture of Experts"), for every token t with
+ * input row h_t:
+ *
+ *   s_i   = W_r[i] . h_t + b_r[i]                       router logits, all E experts
+ *   S_t   = the k largest s_i                            ties: lower expert index wins
+ *   p_i   = exp(s_i) / sum_{j in S_t} exp(s_j)           softmax over the selected set only
+ *   E_i(x)= W_down[i] (silu(W_gate[i] x) * (W_up[i] x))  SwiGLU expert, silu(z) = z/(1+e^-z)
+ *   out_t = sum_{i in S_t} p_i E_i(h_t)
+ *
+ * and the "silent init" expansion of the same page (section 2, Principle and
+ * Proof; section 5.2 for the index convention): every expert and router row is
+ * repeated M times (E' = M E) and k' = M k, which leaves out_t unchanged.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers (HIP device memory of the current
+ *    device), contiguous, row-major, at least 16-byte aligned.  The caller owns
+ *    every buffer; the library never allocates or frees device memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued on it and the call returns after enqueue; results are
+ *    visible after the caller synchronises the stream.
+ *  - Return value: MOE_OK (0) or a negative MOE_ERR_* code.  Argument errors are
+ *    detected before anything is enqueued and leave every output untouched.
+ *    No C++ exception crosses this interface.
+ *  - Calls are independent: concurrent calls are safe when their workspaces
+ *    and outputs do not overlap.
+ */
+#ifndef SMOE_MOE_H
+#define SMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats.
+ *  MOE_F32   IEEE binary32.
+ *  MOE_BF16  bfloat16 (the high 16 bits of a binary32).
+ *  MOE_MXFP4 OCP Microscaling FP4 (expert weights only): E2M1 elements packed
+ *            two per byte — element 2j in the LOW nibble of byte j, element
+ *            2j+1 in the high nibble — and one E8M0 scale byte (value
+ *            2^(x-127)) per group of 32 consecutive elements along the input
+ *            dimension.  Decoded value = E2M1(code) * 2^(scale-127).  This is
+ *            the format the "gpt-oss-20b and gpt-oss-120b" explainer describes
+ *            ("Four-bit expert weights": groups share a scale, 4.25 bits per
+ *            parameter, decoded exactly). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
+
+enum {
+    MOE_OK            = 0,
+    MOE_ERR_NULL      = -1, /* a required pointer is NULL                        */
+    MOE_ERR_SHAPE     = -2, /* sizes outside the supported range (see below)    */
+    MOE_ERR_DTYPE     = -3, /* unsupported (act_dtype, expert_dtype) pair        */
+    MOE_ERR_WORKSPACE = -4, /* workspace smaller than moe_workspace_bytes()      */
+    MOE_ERR_ALIGN     = -5, /* a pointer is not 16-byte aligned                  */
+    MOE_ERR_HIP       = -6, /* the HIP runtime reported an error at enqueue      */
+    MOE_ERR_STATE     = -7  /* profiling calls out of order                      */
+};
+
+/* Problem sizes; field names follow the model configs on the pages
+ * ("openai/gpt-oss-20b" fixture comparison page, Config changes table;
+ * "gpt-oss-220a20b" page, Model Details):
+ *   T  tokens (rows of h)             H  hidden_size
+ *   I  intermediate_size              E  num_local_experts
+ *   k  num_experts_per_tok
+ * Supported: T >= 0 (T = 0 is a no-op), 1 <= k <= E <= 1024, H and I positive
+ * multiples of 64, T*k*max(H,I) < 2^31.
+ * Supported dtype pairs (act_dtype, expert_dtype): (F32, F32), (BF16, BF16),
+ * (BF16, MXFP4).  act_dtype is the format of h, out, w_router and b_router. */
+typedef struct {
+    int32_t T, H, I, E, k;
+    int32_t act_dtype;    /* moe_dtype */
+    int32_t expert_dtype; /* moe_dtype */
+} moe_problem;
+
+/* Layer parameters (device pointers).  Every matrix is [out, in] row-major,
+ * one per expert, experts stacked along the leading dimension:
+ *   w_router [E, H]   act_dtype          b_router [E] act_dtype (NULL = zeros)
+ *   w_gate   [E, I, H]                   w_up     [E, I, H]
+ *   w_down   [E, H, I]
+ * For MXFP4 the three expert tensors are uint8 [E, out, in/2] and the scales
+ * are uint8 s_gate, s_up [E, I, H/32] and s_down [E, H, I/32]; the scale
+ * pointers are ignored for other formats. */
+typedef struct {
+    const void *w_router;
+    const void *b_router;
+    const void *w_gate;
+    const void *w_up;
+    const void *w_down;
+    const uint8_t *s_gate;
+    const uint8_t *s_up;
+    const uint8_t *s_down;
+} moe_weights;
+
+/* Optional routing outputs (device pointers, each may be NULL).
+ *   logits         float [T, E]  s_t,i in fp32
+ *   topk_idx       int32 [T, k]  S_t in ascending expert id
+ *   topk_w         float [T, k]  p_i in the same order (fp32)
+ *   expert_offsets int32 [E+1]   exclusive prefix sum of per-expert counts;
+ *                                expert_offsets[E] = T*k
+ *   perm_src       int32 [T*k]   row r of the expert-major order -> assignment
+ *                                t*k+slot; rows of one expert are ordered by t
+ */
+typedef struct {
+    float   *logits;
+    int32_t *topk_idx;
+    float   *topk_w;
+    int32_t *expert_offsets;
+    int32_t *perm_src;
+} moe_routing;
+
+/* Bytes of device workspace moe_forward needs for problem *p (0 if *p is
+ * invalid).  The workspace holds the routing tables, the expert-major
+ * intermediate activations [T*k, I] and the weighted expert outputs [T*k, H]
+ * in fp32. */
+size_t moe_workspace_bytes(const moe_problem *p);
+
+/* Forward pass of the layer: out[T, H] (act_dtype) from h[T, H] (act_dtype).
+ * Arithmetic: router logits, softmax and all accumulation in fp32; the
+ * intermediate silu(gate)*up activation is stored in act_dtype (rounded to
+ * nearest-even for bf16); the k weighted expert outputs of a token are summed
+ * in fp32 in ascending expert-id order and rounded once to act_dtype.
+ * Deterministic: identical inputs give bitwise-identical outputs.
+ * `routing` may be NULL.  `workspace` must hold moe_workspace_bytes(p) bytes
+ * (16-byte aligned) and must not be used by anything else until the stream
+ * has passed this call.
+ * Errors: MOE_ERR_NULL (p, w, w_router, w_gate, w_up, w_down, h, out or
+ * workspace NULL while T > 0; MXFP4 scales NULL), MOE_ERR_SHAPE, MOE_ERR_DTYPE,
+ * MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP. */
+int moe_forward(const moe_problem *p, const moe_weights *w, const void *h, void *out,
+                const moe_routing *routing, void *workspace, size_t workspace_bytes,
+                void *stream);
+
+/* Silent expansion ("gpt-oss-40b-64a8-init" page, section 2 Principle/Proof,
+ * section 5.2): for every per-expert tensor of *src (w_router, b_router,
+ * w_gate, w_up, w_down and, for MXFP4, the three scale tensors) write
+ * dst row j = src row (j mod E), j = 0 .. M*E-1, so the original experts keep
+ * indices 0..E-1 and their copies follow.  `base` describes the unexpanded
+ * layer (its T is ignored); the caller runs the expanded layer with
+ * E' = M*E and k' = M*k.  Every dst tensor is caller-allocated with M*E rows
+ * and must not overlap its source.  M >= 1 (M = 1 is a plain copy).
+ * b_router may be NULL in both src and dst (then nothing is written for it).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (M < 1, M*E > 1024, invalid base),
+ * MOE_ERR_DTYPE, MOE_ERR_ALIGN, MOE_ERR_HIP. */
+int moe_expand_silent(const moe_problem *base, const moe_weights *src, int32_t M,
+                      const moe_weights *dst, void *stream);
+
+/* Decode MXFP4 weights to bf16 with the same device routine the forward pass
+ * uses when it stages weight tiles.  `packed` holds n_groups runs of 16 bytes
+ * (32 E2M1 codes, element 2j in the low nibble of byte j), `scales` one E8M0
+ * byte per run, `out_bf16` receives n_groups*32 bf16 values.  A whole matrix
+ * [N, K] in the layout of moe_weights is n_groups = N*K/32.  The decode is
+ * exact (every E2M1 value times a power of two in range is a bf16 value;
+ * results beyond the bf16 range become +-inf, scale 255 gives NaN).  Meant for
+ * inspecting and checking stored weights.
+ * Errors: MOE_ERR_SHAPE (n_groups < 0), MOE_ERR_NULL, MOE_ERR_ALIGN (packed or
+ * out_bf16 not 16-byte aligned), MOE_ERR_HIP. */
+int moe_mxfp4_decode(const uint8_t *packed, const uint8_t *scales, int64_t n_groups, void *out_bf16,
+                     void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_string(int status);
+
+/* ---- measurement hooks -------------------------------------------------
+ * Per-stage device timing with HIP events, for benchmarks and profiles.
+ * moe_profile_begin(n) arms recording for the next n moe_forward calls made
+ * from any thread (events are recorded on each call's own stream before and
+ * after every stage); moe_profile_end() waits for those events and returns,
+ * per stage, the summed elapsed milliseconds and the number of calls
+ * recorded.  Stages: 0 router + top-k + softmax, 1 routing scan/permute,
+ * 2 gate/up grouped GEMM with SiLU*up, 3 down grouped GEMM with weighting,
+ * 4 combine.  Errors: MOE_ERR_STATE (begin while armed, end while not armed),
+ * MOE_ERR_SHAPE (n < 1), MOE_ERR_HIP. */
+#define MOE_NUM_STAGES 5
+int moe_profile_begin(int32_t max_calls);
+int moe_profile_end(float stage_ms[MOE_NUM_STAGES], int32_t *calls_recorded);
+const char *moe_stage_name(int stage);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMOE_MOE_H */

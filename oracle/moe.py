@@ -136,13 +136,15 @@ def swiglu_expert(x: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: n
 # ------------------------------------------------------------- the layer --
 
 def moe_forward(h: np.ndarray, weights: LayerWeights, k: int, idx: np.ndarray | None = None,
-                tokens: np.ndarray | None = None) -> dict:
+                tokens: np.ndarray | None = None, workers: int = 1) -> dict:
     """The layer, evaluated expert by expert.
 
     ``h`` is float64 ``[T, H]``.  Routing (logits, selection, weights) is done
     for every token; outputs are formed for ``tokens`` (default: all).
     ``idx`` replaces the selection (it must be a valid top-k set per token; the
-    parity check passes one only to settle near-ties).
+    parity check passes one only to settle near-ties).  ``workers > 1``
+    evaluates experts on that many threads; their contributions are still
+    added in ascending expert order.
 
     Returns ``out`` (``[len(tokens), H]``), ``s``, ``idx``, ``p``, ``gap``.
     """
@@ -160,13 +162,27 @@ def moe_forward(h: np.ndarray, weights: LayerWeights, k: int, idx: np.ndarray | 
     sub_idx = idx[tokens]
     sub_p = p[tokens]
     out = np.zeros((len(tokens), h.shape[1]))
-    for e in range(E):
+
+    def contribution(e):
         rows, slots = np.nonzero(sub_idx == e)
         if rows.size == 0:
-            continue
+            return rows, None
         wg, wu, wd = weights.expert(e)
         y = swiglu_expert(h[tokens[rows]], wg, wu, wd)
-        np.add.at(out, rows, sub_p[rows, slots][:, None] * y)
+        return rows, sub_p[rows, slots][:, None] * y
+
+    if workers > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(workers) as ex:
+            parts = ex.map(contribution, range(E))
+            for rows, c in parts:
+                if c is not None:
+                    np.add.at(out, rows, c)
+    else:
+        for e in range(E):
+            rows, c = contribution(e)
+            if c is not None:
+                np.add.at(out, rows, c)
     return {"out": out, "s": s, "idx": idx, "p": p, "gap": gap}
 
 

@@ -1,0 +1,53 @@
+// Stage 4 of the layer: the weighted sum over the selected experts
+// ("gpt-oss-40b-64a8-init" page, section 2, Proof: FFN(h) = sum p_i E_i(h)).
+// The down stage already multiplied each expert output by its weight p_i and
+// stored it at the assignment's slot, so
+//     out[t, :] = y[t*k + 0, :] + y[t*k + 1, :] + ... + y[t*k + k-1, :]
+// summed in fp32 in slot order (= ascending expert id), rounded once.
+// Memory bound: 4 outputs per thread, 16-byte loads.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, void* __restrict__ out, int T,
+                                                      int H, int k) {
+    const int h4 = H >> 2;
+    const size_t n4 = (size_t)T * h4;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+        const size_t t = i / h4;
+        const size_t c = i % h4;
+        const float4* src = reinterpret_cast<const float4*>(y) + (t * k) * h4 + c;
+        float4 acc = src[0];
+        for (int s = 1; s < k; ++s) {
+            const float4 v = src[(size_t)s * h4];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        if constexpr (kBf16Out) {
+            uint2 o;
+            o.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
+            o.y = f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16);
+            reinterpret_cast<uint2*>(out)[i] = o;
+        } else {
+            reinterpret_cast<float4*>(out)[i] = acc;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k, hipStream_t stream) {
+    const size_t n4 = (size_t)T * (H / 4);
+    const int blocks = (int)((n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192);
+    if (act_dtype == DT_BF16)
+        combine_kernel<true><<<blocks, 256, 0, stream>>>(y, out, T, H, k);
+    else
+        combine_kernel<false><<<blocks, 256, 0, stream>>>(y, out, T, H, k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,283 @@
+// C interface of the sparse MoE layer (declared in include/moe.h): argument
+// checks, workspace layout, stage launches on the caller's stream, the silent
+// expansion and the per-stage timing hooks.
+#include <mutex>
+#include <vector>
+
+#include "../../include/moe.h"
+#include "moe_internal.h"
+
+namespace {
+
+using moe::Tile;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+int check_problem(const moe_problem* p) {
+    if (!p) return MOE_ERR_NULL;
+    if (p->T < 0 || p->H <= 0 || p->I <= 0 || p->E < 1 || p->E > 1024 || p->k < 1 || p->k > p->E)
+        return MOE_ERR_SHAPE;
+    if (p->H % 64 != 0 || p->I % 64 != 0) return MOE_ERR_SHAPE;
+    const int64_t big = (int64_t)p->T * p->k * (p->H > p->I ? p->H : p->I);
+    if (big >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+    const bool ok = (p->act_dtype == MOE_F32 && p->expert_dtype == MOE_F32) ||
+                    (p->act_dtype == MOE_BF16 && (p->expert_dtype == MOE_BF16 || p->expert_dtype == MOE_MXFP4));
+    if (!ok) return MOE_ERR_DTYPE;
+    return MOE_OK;
+}
+
+// Workspace regions, in order.
+struct Layout {
+    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, act, y, total;
+    int nblk, max_tiles, BM;
+};
+
+Layout layout(const moe_problem* p) {
+    Layout L{};
+    const size_t tk = (size_t)p->T * p->k;
+    L.BM = moe::gemm_block_m(p->act_dtype, p->expert_dtype, p->T, p->k, p->E);
+    L.nblk = (p->T + moe::kRouterTokens - 1) / moe::kRouterTokens;
+    L.max_tiles = (int)((tk + L.BM - 1) / L.BM) + p->E;
+    size_t o = 0;
+    L.topk_idx = o; o = align_up(o + tk * 4);
+    L.topk_w = o;   o = align_up(o + tk * 4);
+    L.blk = o;      o = align_up(o + (size_t)p->E * L.nblk * 4);
+    L.rank = o;     o = align_up(o + tk * 4);
+    L.offsets = o;  o = align_up(o + ((size_t)p->E + 1) * 4);
+    L.perm = o;     o = align_up(o + tk * 4);
+    L.inv = o;      o = align_up(o + tk * 4);
+    L.tiles = o;    o = align_up(o + (size_t)L.max_tiles * sizeof(Tile));
+    L.ntiles = o;   o = align_up(o + 4);
+    L.act = o;      o = align_up(o + tk * p->I * act_bytes(p->act_dtype));
+    L.y = o;        o = align_up(o + tk * p->H * 4);
+    L.total = o;
+    return L;
+}
+
+// ------------------------------------------------------------ profiling --
+struct Profiler {
+    std::mutex mu;
+    bool armed = false;
+    int max_calls = 0;
+    int used = 0;
+    std::vector<hipEvent_t> ev;  // max_calls x (MOE_NUM_STAGES + 1)
+};
+Profiler& prof() {
+    static Profiler p;
+    return p;
+}
+
+// Returns the event row for this call, or nullptr when not recording.
+hipEvent_t* prof_slot() {
+    Profiler& P = prof();
+    std::lock_guard<std::mutex> g(P.mu);
+    if (!P.armed || P.used >= P.max_calls) return nullptr;
+    return &P.ev[(size_t)(P.used++) * (MOE_NUM_STAGES + 1)];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_problem* p) {
+    if (check_problem(p) != MOE_OK) return 0;
+    return layout(p).total;
+}
+
+const char* moe_status_string(int s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_NULL: return "required pointer is NULL";
+        case MOE_ERR_SHAPE: return "unsupported sizes (need 0<=T, 1<=k<=E<=1024, H and I positive multiples of 64, T*k*max(H,I) < 2^31, M>=1)";
+        case MOE_ERR_DTYPE: return "unsupported dtype pair (need F32/F32, BF16/BF16 or BF16/MXFP4)";
+        case MOE_ERR_WORKSPACE: return "workspace smaller than moe_workspace_bytes()";
+        case MOE_ERR_ALIGN: return "pointer not aligned (16 bytes for tensors and workspace, 4 for routing outputs and bias)";
+        case MOE_ERR_HIP: return "HIP runtime error at enqueue";
+        case MOE_ERR_STATE: return "profiling calls out of order";
+        default: return "unknown status";
+    }
+}
+
+const char* moe_stage_name(int s) {
+    static const char* names[MOE_NUM_STAGES] = {"router_topk_softmax", "route_scan_permute", "gateup_swiglu_gemm",
+                                                "down_weighted_gemm", "combine"};
+    return (s >= 0 && s < MOE_NUM_STAGES) ? names[s] : "unknown";
+}
+
+int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void* out, const moe_routing* routing,
+                void* workspace, size_t workspace_bytes, void* stream_v) {
+    int st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!w) return MOE_ERR_NULL;
+    if (p->T == 0) return MOE_OK;
+    if (!h || !out || !workspace || !w->w_router || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
+    if (p->expert_dtype == MOE_MXFP4 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL;
+    for (const void* q : {h, (const void*)out, (const void*)workspace, w->w_router, w->w_gate, w->w_up, w->w_down})
+        if (!aligned(q, 16)) return MOE_ERR_ALIGN;
+    if (w->b_router && !aligned(w->b_router, act_bytes(p->act_dtype))) return MOE_ERR_ALIGN;
+    if (routing) {
+        for (const void* q : {(const void*)routing->logits, (const void*)routing->topk_idx,
+                              (const void*)routing->topk_w, (const void*)routing->expert_offsets,
+                              (const void*)routing->perm_src})
+            if (q && !aligned(q, 4)) return MOE_ERR_ALIGN;
+    }
+    const Layout L = layout(p);
+    if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    char* ws = reinterpret_cast<char*>(workspace);
+    int32_t* topk_idx = (routing && routing->topk_idx) ? routing->topk_idx : (int32_t*)(ws + L.topk_idx);
+    float* topk_w = (routing && routing->topk_w) ? routing->topk_w : (float*)(ws + L.topk_w);
+    int32_t* offsets = (routing && routing->expert_offsets) ? routing->expert_offsets : (int32_t*)(ws + L.offsets);
+    int32_t* perm = (routing && routing->perm_src) ? routing->perm_src : (int32_t*)(ws + L.perm);
+    float* logits = routing ? routing->logits : nullptr;
+    int32_t* blk = (int32_t*)(ws + L.blk);
+    int32_t* rank = (int32_t*)(ws + L.rank);
+    int32_t* inv = (int32_t*)(ws + L.inv);
+    Tile* tiles = (Tile*)(ws + L.tiles);
+    int32_t* ntiles = (int32_t*)(ws + L.ntiles);
+    void* act = ws + L.act;
+    float* y = (float*)(ws + L.y);
+
+    hipEvent_t* ev = prof_slot();
+    auto mark = [&](int i) {
+        if (ev) (void)hipEventRecord(ev[i], stream);
+    };
+
+    hipError_t e = hipSuccess;
+    mark(0);
+    e = moe::launch_router(p->act_dtype, h, w->w_router, w->b_router, p->T, p->H, p->E, p->k, logits, topk_idx,
+                           topk_w, blk, rank, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(1);
+    e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
+                               L.max_tiles, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(2);
+
+    moe::GemmProblem g{};
+    g.T = p->T; g.H = p->H; g.I = p->I; g.E = p->E; g.k = p->k;
+    g.act_dtype = p->act_dtype;
+    g.expert_dtype = p->expert_dtype;
+    g.h = h;
+    g.w_gate = w->w_gate; g.w_up = w->w_up; g.w_down = w->w_down;
+    g.s_gate = w->s_gate; g.s_up = w->s_up; g.s_down = w->s_down;
+    g.perm_src = perm;
+    g.topk_w = topk_w;
+    g.tiles = tiles;
+    g.n_tiles = ntiles;
+    g.max_tiles = L.max_tiles;
+    g.act = act;
+    g.y = y;
+    e = moe::launch_gateup(g, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(3);
+    e = moe::launch_down(g, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(4);
+    e = moe::launch_combine(p->act_dtype, y, out, p->T, p->H, p->k, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(5);
+    return MOE_OK;
+}
+
+int moe_expand_silent(const moe_problem* base, const moe_weights* src, int32_t M, const moe_weights* dst,
+                      void* stream_v) {
+    if (!base || !src || !dst) return MOE_ERR_NULL;
+    moe_problem q = *base;
+    q.T = 0;
+    int st = check_problem(&q);
+    if (st != MOE_OK) return st;
+    if (M < 1 || (int64_t)M * base->E > 1024) return MOE_ERR_SHAPE;
+    const bool mx = base->expert_dtype == MOE_MXFP4;
+    const size_t E = base->E, H = base->H, I = base->I;
+    const size_t ab = act_bytes(base->act_dtype);
+    const size_t eb = base->expert_dtype == MOE_F32 ? 4 : 2;
+
+    struct T_ {
+        const void* s;
+        void* d;
+        size_t row_bytes;
+        bool required;
+    };
+    std::vector<T_> list = {
+        {src->w_router, (void*)dst->w_router, H * ab, true},
+        {src->b_router, (void*)dst->b_router, ab, false},
+        {src->w_gate, (void*)dst->w_gate, mx ? I * H / 2 : I * H * eb, true},
+        {src->w_up, (void*)dst->w_up, mx ? I * H / 2 : I * H * eb, true},
+        {src->w_down, (void*)dst->w_down, mx ? H * I / 2 : H * I * eb, true},
+    };
+    if (mx) {
+        list.push_back({src->s_gate, (void*)dst->s_gate, I * H / 32, true});
+        list.push_back({src->s_up, (void*)dst->s_up, I * H / 32, true});
+        list.push_back({src->s_down, (void*)dst->s_down, H * I / 32, true});
+    }
+    for (const T_& t : list) {
+        if (t.required && (!t.s || !t.d)) return MOE_ERR_NULL;
+        if (!t.required && ((t.s == nullptr) != (t.d == nullptr))) return MOE_ERR_NULL;
+    }
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    for (const T_& t : list) {
+        if (!t.s) continue;
+        const size_t bytes = E * t.row_bytes;
+        for (int m = 0; m < M; ++m) {
+            if (hipMemcpyAsync(static_cast<char*>(t.d) + (size_t)m * bytes, t.s, bytes, hipMemcpyDeviceToDevice,
+                               stream) != hipSuccess)
+                return MOE_ERR_HIP;
+        }
+    }
+    return MOE_OK;
+}
+
+int moe_profile_begin(int32_t max_calls) {
+    if (max_calls < 1) return MOE_ERR_SHAPE;
+    Profiler& P = prof();
+    std::lock_guard<std::mutex> g(P.mu);
+    if (P.armed) return MOE_ERR_STATE;
+    P.ev.assign((size_t)max_calls * (MOE_NUM_STAGES + 1), nullptr);
+    for (auto& e : P.ev)
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (auto& x : P.ev)
+                if (x) (void)hipEventDestroy(x);
+            P.ev.clear();
+            return MOE_ERR_HIP;
+        }
+    P.max_calls = max_calls;
+    P.used = 0;
+    P.armed = true;
+    return MOE_OK;
+}
+
+int moe_profile_end(float stage_ms[MOE_NUM_STAGES], int32_t* calls_recorded) {
+    Profiler& P = prof();
+    std::lock_guard<std::mutex> g(P.mu);
+    if (!P.armed) return MOE_ERR_STATE;
+    int rc = MOE_OK;
+    float sums[MOE_NUM_STAGES] = {0};
+    for (int c = 0; c < P.used; ++c) {
+        hipEvent_t* row = &P.ev[(size_t)c * (MOE_NUM_STAGES + 1)];
+        if (hipEventSynchronize(row[MOE_NUM_STAGES]) != hipSuccess) rc = MOE_ERR_HIP;
+        for (int s = 0; s < MOE_NUM_STAGES; ++s) {
+            float ms = 0.f;
+            if (hipEventElapsedTime(&ms, row[s], row[s + 1]) != hipSuccess) rc = MOE_ERR_HIP;
+            sums[s] += ms;
+        }
+    }
+    if (stage_ms)
+        for (int s = 0; s < MOE_NUM_STAGES; ++s) stage_ms[s] = sums[s];
+    if (calls_recorded) *calls_recorded = P.used;
+    for (auto& e : P.ev) (void)hipEventDestroy(e);
+    P.ev.clear();
+    P.armed = false;
+    P.used = 0;
+    P.max_calls = 0;
+    return rc;
+}
+
+}  // extern "C"

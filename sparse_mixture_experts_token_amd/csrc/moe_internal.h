@@ -1,0 +1,163 @@
+// Internal declarations shared by the HIP translation units of libmoe.
+// gfx950 (CDNA4) only: wave64, MFMA bf16/f32, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ----------------------------------------------------------------- types --
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+enum : int { DT_F32 = 0, DT_BF16 = 1, DT_MXFP4 = 2 };
+
+// Router/top-k tile: tokens per workgroup.
+constexpr int kRouterTokens = 16;
+
+// One row-tile of one expert in the expert-major order (built on the device).
+struct Tile {
+    int32_t expert;
+    int32_t row_start;  // first row (expert-major order)
+    int32_t rows;       // valid rows, 1..BM
+    int32_t pad;
+};
+
+// ------------------------------------------------------ bf16 conversions --
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest, ties to even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// ------------------------------------------------------------ MXFP4 -> bf16 --
+// Exact decode of one E2M1 code with an E8M0 scale into bf16 bits, in integer
+// arithmetic.  Magnitude code c = (e, m) with e = c>>1, m = c&1 is
+// 2^(e-1) (1 + m/2) for e > 0 and m/2 for e = 0, so the scaled value
+// 2^(scale-127) * E2M1(c) has bf16 exponent field  e + scale - 1  (e > 0) or
+// scale - 1 (c = 1, significand 1.0) and mantissa top bit m.  Fields <= 0 give
+// bf16 subnormals (exact: at most a 2-bit shift of a 2-bit significand),
+// fields >= 255 overflow to infinity; scale 255 is NaN.
+__device__ __forceinline__ uint32_t e2m1_to_bf16_exact(uint32_t code, uint32_t scale) {
+    const uint32_t sign = (code & 8u) << 12;
+    const uint32_t mag = code & 7u;
+    if (scale == 255u) return 0x7fc0u | sign;
+    if (mag == 0u) return sign;
+    const int e = (int)(mag >> 1);
+    const uint32_t mbit = mag >= 2u ? ((mag & 1u) << 6) : 0u;
+    const int field = (mag >= 2u ? e : 0) + (int)scale - 1;
+    if (field >= 255) return 0x7f80u | sign;
+    if (field >= 1) return sign | ((uint32_t)field << 7) | mbit;
+    return sign | ((0x80u | mbit) >> (1 - field));  // subnormal, field in {-1, 0}
+}
+
+// Decode 32 MXFP4 elements (16 packed bytes, element 2j in the low nibble of
+// byte j) sharing one E8M0 scale into 32 bf16 (two per output word, element
+// 2j in the low half).  Scales 2..252 use the hardware scaled FP4->BF16
+// conversion (the product is a power-of-two scaling of a 2-bit significand,
+// so it is exact); the other scales take the exact integer path.
+__device__ __forceinline__ uint32_t cvt_fp4x2_bf16x2(uint32_t w, float sc, int byte) {
+    typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+    bf16x2 v;
+    switch (byte) {  // the byte selector must be an immediate
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3); break;
+    }
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ void decode_mxfp4_32(const uint4& q, uint32_t scale, uint32_t out[16]) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    if (scale >= 2u && scale <= 252u) {
+        const float sc = __uint_as_float(scale << 23);  // 2^(scale-127), a normal float
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b) out[i * 4 + b] = cvt_fp4x2_bf16x2(w[i], sc, b);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t byte = (w[i] >> (8 * b)) & 0xffu;
+                out[i * 4 + b] = e2m1_to_bf16_exact(byte & 0xfu, scale) | (e2m1_to_bf16_exact(byte >> 4, scale) << 16);
+            }
+    }
+}
+
+// ------------------------------------------------------------- MFMA wrappers --
+// 32x32x16 bf16: lane l holds A[l%32][8(l/32)+0..7], B[8(l/32)+0..7][l%32];
+// D[4i+j] is row 8i+4(l/32)+j, column l%32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// 32x32x2 f32: lane l holds A[l%32][l/32], B[l/32][l%32]; same D layout.
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+// 16x16x32 bf16: lane l holds A[l%16][8(l/16)+0..7], B[8(l/16)+0..7][l%16];
+// D[j] is row 4(l/16)+j, column l%16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// 16x16x4 f32: lane l holds A[l%16][l/16], B[l/16][l%16]; same D layout.
+__device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// -------------------------------------------------------------- launchers --
+// All launchers enqueue on `stream` and return hipGetLastError().
+
+// Stage 0: router logits + top-k + selected softmax + per-tile counts/ranks.
+hipError_t launch_router(int act_dtype, const void* h, const void* w_router, const void* b_router,
+                         int T, int H, int E, int k, float* logits_opt, int32_t* topk_idx,
+                         float* topk_w, int32_t* blk_counts /*[E][nblk]*/, int32_t* local_rank,
+                         hipStream_t stream);
+
+// Stage 1: scan + stable permutation + tile list.
+hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx,
+                             int32_t* blk_counts /*in: counts, out: bases*/,
+                             const int32_t* local_rank, int32_t* offsets /*[E+1]*/,
+                             int32_t* perm_src, int32_t* inv, Tile* tiles, int32_t* n_tiles,
+                             int max_tiles, hipStream_t stream);
+
+// Stages 2 and 3: grouped GEMMs over the tile list.
+struct GemmProblem {
+    int T, H, I, E, k;
+    int act_dtype, expert_dtype;
+    const void* h;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+    const uint8_t* s_gate;
+    const uint8_t* s_up;
+    const uint8_t* s_down;
+    const int32_t* perm_src;
+    const float* topk_w;
+    const Tile* tiles;
+    const int32_t* n_tiles;
+    int max_tiles;
+    void* act;  // [T*k, I] act_dtype (expert-major rows)
+    float* y;   // [T*k, H] fp32, indexed by assignment t*k+slot
+};
+int gemm_block_m(int act_dtype, int expert_dtype, int T, int k, int E);
+hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_down(const GemmProblem& p, hipStream_t stream);
+
+// Stage 4: out[t] = sum_slot y[t*k+slot] (fp32, slot order), rounded to act dtype.
+hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k,
+                          hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,126 @@
+// Stage 1 of the layer: from the per-token selected sets to the expert-major
+// order in which the experts' rows are processed.
+//
+//   counts[e]   number of (token, slot) assignments to expert e
+//   offsets     exclusive prefix sum of counts, offsets[E] = T*k
+//   perm_src[r] the assignment t*k+slot at row r; rows of one expert are
+//               ordered by token (a stable counting sort: no atomics, so the
+//               result is unique and run-to-run identical)
+//   inv[a]      the row of assignment a
+//   tiles       the (expert, first row, rows) tiles of at most BM rows that the
+//               grouped GEMMs walk; experts without tokens get no tile.
+//
+// One workgroup of 1024 threads.  Input: the per-token-tile expert counts and
+// the within-tile ranks written by the router stage.
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    return x;
+}
+
+__global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, int BM,
+                                                          const int32_t* __restrict__ topk_idx,
+                                                          int32_t* __restrict__ blk,  // [E][nblk]
+                                                          const int32_t* __restrict__ local_rank,
+                                                          int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
+                                                          int32_t* __restrict__ inv, Tile* __restrict__ tiles,
+                                                          int32_t* __restrict__ n_tiles, int max_tiles) {
+    __shared__ int32_t totals[1024];
+    __shared__ int32_t offs[1025];
+    __shared__ int32_t toff[1025];
+    __shared__ int32_t wsum[16];
+    __shared__ int32_t wtile[16];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int nblk = (T + kRouterTokens - 1) / kRouterTokens;
+
+    // 1. per expert: exclusive scan of its tile counts (in place) and its total
+    for (int e = wave; e < E; e += 16) {
+        int running = 0;
+        int32_t* row = blk + (size_t)e * nblk;
+        for (int b0 = 0; b0 < nblk; b0 += 64) {
+            const int i = b0 + lane;
+            const int c = i < nblk ? row[i] : 0;
+            const int x = wave_incl_scan(c, lane);
+            if (i < nblk) row[i] = running + x - c;
+            running += __shfl(x, 63, 64);
+        }
+        if (lane == 0) totals[e] = running;
+    }
+    __syncthreads();
+
+    // 2. exclusive scans over experts: row offsets and tile offsets
+    const int cnt = tid < E ? totals[tid] : 0;
+    const int nt = tid < E ? (cnt + BM - 1) / BM : 0;
+    int xs = wave_incl_scan(cnt, lane);
+    int xt = wave_incl_scan(nt, lane);
+    if (lane == 63) {
+        wsum[wave] = xs;
+        wtile[wave] = xt;
+    }
+    __syncthreads();
+    int bs = 0, bt = 0;
+    for (int w = 0; w < wave; ++w) {
+        bs += wsum[w];
+        bt += wtile[w];
+    }
+    if (tid < E) {
+        offs[tid] = bs + xs - cnt;
+        toff[tid] = bt + xt - nt;
+    }
+    if (tid == E - 1) {
+        offs[E] = bs + xs;
+        toff[E] = bt + xt;
+    }
+    __syncthreads();
+
+    // 3. outputs: offsets and the tile list
+    if (tid < E) offsets[tid] = offs[tid];
+    if (tid == 0) {
+        offsets[E] = offs[E];
+        n_tiles[0] = toff[E];
+    }
+    if (tid < E) {
+        const int base = toff[tid];
+        for (int j = 0; j < nt && base + j < max_tiles; ++j) {
+            Tile tl;
+            tl.expert = tid;
+            tl.row_start = offs[tid] + j * BM;
+            tl.rows = min(BM, cnt - j * BM);
+            tl.pad = 0;
+            tiles[base + j] = tl;
+        }
+    }
+
+    // 4. stable scatter: row = offsets[e] + (earlier tiles' count) + rank in tile
+    const int total = T * k;
+    for (int a = tid; a < total; a += 1024) {
+        const int e = topk_idx[a];
+        const int b = (a / k) / kRouterTokens;
+        const int r = offs[e] + blk[(size_t)e * nblk + b] + local_rank[a];
+        perm_src[r] = a;
+        inv[a] = r;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx, int32_t* blk_counts,
+                             const int32_t* local_rank, int32_t* offsets, int32_t* perm_src, int32_t* inv,
+                             Tile* tiles, int32_t* n_tiles, int max_tiles, hipStream_t stream) {
+    route_scan_kernel<<<1, 1024, 0, stream>>>(T, E, k, BM, topk_idx, blk_counts, local_rank, offsets, perm_src, inv,
+                                              tiles, n_tiles, max_tiles);
+    return hipGetLastError();
+}
+
+}  // namespace moe

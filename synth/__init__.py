@@ -206,11 +206,12 @@ class Layer:
         return arrs
 
 
-def make_layer(key: int, T: int | None = None, hot_beta: float | None = None) -> Layer:
-    """Inputs of workload ``key`` (a key of ``CONFIGS``) with the first ``T``
-    tokens (default: the workload's prefill T).  ``hot_beta`` overrides the
-    hot experts' router-bias offset (used only to choose that offset)."""
-    c = CONFIGS[key]
+def make_layer(key, T: int | None = None, hot_beta: float | None = None) -> Layer:
+    """Inputs of workload ``key`` (a key of ``CONFIGS``, or a ``Config`` for
+    an extra shape) with the first ``T`` tokens (default: the workload's
+    prefill T).  ``hot_beta`` overrides the hot experts' router-bias offset
+    (used only to choose that offset)."""
+    c = key if isinstance(key, Config) else CONFIGS[key]
     beta = c.hot_beta if hot_beta is None else hot_beta
     T = c.T if T is None else T
     if T > c.T:

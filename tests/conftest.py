@@ -26,3 +26,13 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_test(request):
+    # Name the case on the real stderr (not captured) before any GPU work, so
+    # that a run that dies inside a kernel still says which case it was.
+    if "gpu" in request.node.keywords:
+        sys.__stderr__.write(f"\n[gpu-test] start {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,99 @@
+"""The C interface without a GPU: the library loads, exports every function
+include/moe.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_token_amd as smoe
+
+HEADER = os.path.join(os.path.dirname(__file__), "..", "include", "moe.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = smoe.load()
+    names = declared_functions()
+    assert len(names) == 8, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(smoe.EXPORTED) == names
+
+
+def test_status_strings():
+    for code in range(-7, 1):
+        assert smoe.moe_status_string(code) and smoe.moe_status_string(code) != "unknown status"
+    assert smoe.moe_status_string(-99) == "unknown status"
+    assert smoe.moe_stage_name(2) == "gateup_swiglu_gemm"
+
+
+def _ws(**kw):
+    base = dict(T=16, H=64, I=128, E=4, k=2, act_dtype=smoe.MOE_F32, expert_dtype=smoe.MOE_F32)
+    base.update(kw)
+    return smoe.moe_workspace_bytes(smoe.Problem(**base))
+
+
+def test_workspace_size_and_shape_limits():
+    assert _ws() > 0
+    assert _ws(T=32) > _ws(T=16)
+    assert _ws(T=0) > 0
+    for bad in (dict(k=0), dict(k=5), dict(E=0), dict(E=1025, k=2), dict(H=96), dict(I=100), dict(T=-1),
+                dict(act_dtype=smoe.MOE_BF16, expert_dtype=smoe.MOE_F32), dict(expert_dtype=smoe.MOE_MXFP4),
+                dict(T=1 << 20, k=4, H=1024)):
+        assert _ws(**bad) == 0, bad
+    assert _ws(E=1024, k=1024, T=2) > 0
+    assert _ws(act_dtype=smoe.MOE_BF16, expert_dtype=smoe.MOE_MXFP4) > 0
+
+
+def _call(problem, weights=None, h=0x1000, out=0x2000, ws=0x3000, ws_bytes=1 << 40):
+    lib = smoe.load()
+    w = smoe._Weights(*[weights.get(n) if weights else 0x4000 for n in smoe._WEIGHT_FIELDS])
+    p = problem._c() if problem is not None else None
+    return lib.moe_forward(ctypes.byref(p) if p is not None else None, ctypes.byref(w), h, out, None, ws,
+                           ws_bytes, None)
+
+
+def test_forward_argument_errors_return_before_any_launch():
+    P = smoe.Problem(16, 64, 128, 4, 2, smoe.MOE_F32, smoe.MOE_F32)
+    assert _call(None) == -1
+    assert _call(smoe.Problem(16, 64, 128, 4, 5, smoe.MOE_F32, smoe.MOE_F32)) == -2
+    assert _call(smoe.Problem(16, 64, 128, 4, 2, smoe.MOE_F32, smoe.MOE_BF16)) == -3
+    assert _call(P, h=0) == -1
+    assert _call(P, h=0x1004) == -5
+    assert _call(P, ws_bytes=16) == -4
+    w = {n: 0x4000 for n in smoe._WEIGHT_FIELDS}
+    w["w_down"] = 0
+    assert _call(P, weights=w) == -1
+    mx = smoe.Problem(16, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_MXFP4)
+    w = {n: 0x4000 for n in smoe._WEIGHT_FIELDS}
+    w["s_up"] = 0
+    assert _call(mx, weights=w) == -1
+    # T = 0 is a no-op even with no buffers at all
+    assert _call(smoe.Problem(0, 64, 128, 4, 2, smoe.MOE_F32, smoe.MOE_F32), h=0, out=0, ws=0, ws_bytes=0) == 0
+
+
+def test_expand_and_decode_argument_errors():
+    lib = smoe.load()
+    P = smoe.Problem(0, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_BF16)._c()
+    w = smoe._Weights(*([0x4000] * 8))
+    assert lib.moe_expand_silent(ctypes.byref(P), ctypes.byref(w), 0, ctypes.byref(w), None) == -2
+    assert lib.moe_expand_silent(ctypes.byref(P), ctypes.byref(w), 257, ctypes.byref(w), None) == -2
+    w0 = smoe._Weights(*([0] * 8))
+    assert lib.moe_expand_silent(ctypes.byref(P), ctypes.byref(w0), 2, ctypes.byref(w), None) == -1
+    assert lib.moe_expand_silent(None, ctypes.byref(w), 2, ctypes.byref(w), None) == -1
+    assert lib.moe_mxfp4_decode(0x1000, 0x2000, -1, 0x3000, None) == -2
+    assert lib.moe_mxfp4_decode(0, 0x2000, 4, 0x3000, None) == -1
+    assert lib.moe_mxfp4_decode(0x1008, 0x2000, 4, 0x3000, None) == -5
+    assert lib.moe_mxfp4_decode(0, 0, 0, 0, None) == 0
+
+
+def test_profile_end_without_begin_is_a_state_error():
+    lib = smoe.load()
+    assert lib.moe_profile_end(None, None) == -7
+    assert lib.moe_profile_begin(0) == -2

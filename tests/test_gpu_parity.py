@@ -1,0 +1,251 @@
+"""Parity of the HIP path (through the C interface) with the fp64 reference.
+
+Routing (top-k indices in ascending expert id, offsets, permutation) must be
+bit-exact once near-ties (k-th and (k+1)-th reference logits within 1e-5) are
+settled; outputs must be within relative L2 5e-3 and max abs 1e-2*max|ref| for
+bf16/MXFP4 and relative L2 1e-5 for fp32.  Sizes that the reference finishes
+in seconds are compared element by element; full-size workloads on sampled
+tokens (routing is always checked on every token)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_token_amd as smoe
+import synth
+from gpu_util import (check_layer, check_out, device_weights, oracle_weights, problem, rel_l2, run, to_dev,
+                      workers)
+
+pytestmark = pytest.mark.gpu
+
+_cache = {}
+
+
+def layer_full(key):
+    """Seeded inputs of a workload at its full T, weights stacked (cached)."""
+    if key not in _cache:
+        L = synth.make_layer(key)
+        _cache[key] = (L, L.stacked())
+    return _cache[key]
+
+
+def with_T(L: synth.Layer, T: int) -> synth.Layer:
+    return dataclasses.replace(L, T=T, h=L.h[:T])
+
+
+def sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(T, size=min(n, T), replace=False))
+
+
+# ------------------------------------------------------------ small sizes --
+
+def test_fixture_fp32_all_tokens():
+    L, st = layer_full(1)
+    m, _ = check_layer(L, st)
+    assert m["rel_l2"] < 1e-5
+
+
+@pytest.mark.parametrize("T", [1, 7, 17, 33])
+def test_fixture_fp32_ragged_T(T):
+    L, st = layer_full(1)
+    check_layer(with_T(L, T), st)
+
+
+EDGE = [
+    synth.Config(101, "ragged-7e-top3", T=333, H=128, I=192, E=7, k=3, act="bf16", expert="bf16"),
+    synth.Config(102, "top1", T=100, H=64, I=64, E=5, k=1, act="bf16", expert="bf16"),
+    synth.Config(103, "k-equals-E", T=50, H=64, I=128, E=6, k=6, act="bf16", expert="bf16"),
+    synth.Config(104, "single-expert", T=40, H=64, I=64, E=1, k=1, act="bf16", expert="bf16"),
+    synth.Config(105, "mostly-empty-experts", T=3, H=128, I=128, E=64, k=2, act="bf16", expert="bf16"),
+    synth.Config(106, "mxfp4-small", T=200, H=128, I=256, E=9, k=2, act="bf16", expert="mxfp4"),
+    synth.Config(107, "f32-tails", T=77, H=192, I=320, E=5, k=2, act="f32", expert="f32", bias_std=0.01),
+    synth.Config(108, "many-tiles-per-expert", T=1500, H=64, I=128, E=3, k=2, act="bf16", expert="bf16"),
+    synth.Config(109, "1024-experts", T=40, H=64, I=64, E=1024, k=9, act="bf16", expert="bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
+def test_edge_shapes(cfg):
+    L = synth.make_layer(cfg)
+    check_layer(L, L.stacked())
+
+
+def test_gpt_oss_20b_layer_2048_tokens_all_outputs():
+    """Several row tiles per expert and a ragged last tile, all tokens compared."""
+    L, st = layer_full(2)
+    m, _ = check_layer(with_T(L, 2048), st)
+    print(m)
+
+
+def test_gpt_oss_20b_decode_64_tokens():
+    L, st = layer_full(2)
+    check_layer(with_T(L, 64), st)
+
+
+def test_deterministic_run_to_run():
+    L, st = layer_full(2)
+    prob = problem(L.cfg, 512)
+    w = device_weights(L, st)
+    h = to_dev(L.h[:512], "bf16")
+    a = run(prob, w, h, "bf16")
+    b = run(prob, w, h, "bf16")
+    assert torch.equal(a["out_raw"].view(torch.int16), b["out_raw"].view(torch.int16))
+    for n in ("logits", "topk_idx", "topk_w", "perm_src"):
+        np.testing.assert_array_equal(a[n], b[n])
+
+
+# --------------------------------------------------------------- full sizes --
+
+def test_gpt_oss_20b_prefill_4096_sampled():
+    L, st = layer_full(2)
+    m, _ = check_layer(L, st, tokens=sample_tokens(L.T, 256, 2))
+    print(m)
+
+
+@pytest.mark.parametrize("M", [2, 3])
+def test_silent_expansion_identity(M):
+    """64a8 / 96a12: the expanded layer equals the 32a4 layer (GPU vs GPU and
+    GPU vs the fp64 reference), copies of a router row give bitwise-equal
+    logits, and the selected set is the copies of the base selection."""
+    L, st = layer_full(2)
+    c = L.cfg
+    base = problem(c, L.T)
+    w = device_weights(L, st)
+    big = smoe.Problem(L.T, c.H, c.I, M * c.E, M * c.k, base.act_dtype, base.expert_dtype)
+    wx = {n: torch.empty((M * t.shape[0],) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+          for n, t in w.items()}
+    smoe.moe_expand_silent(base, w, M, wx)
+    torch.cuda.synchronize()
+    for n in w:
+        for m in range(M):
+            assert torch.equal(wx[n][m * c.E:(m + 1) * c.E], w[n])
+    h = to_dev(L.h, "bf16")
+    gb = run(base, w, h, "bf16")
+    gx = run(big, wx, h, "bf16")
+    # duplicated router rows: bitwise-equal logits
+    for m in range(1, M):
+        np.testing.assert_array_equal(gx["logits"][:, m * c.E:(m + 1) * c.E], gx["logits"][:, :c.E])
+    np.testing.assert_array_equal(gx["logits"][:, :c.E], gb["logits"])
+    # selection: the M copies of each base choice (ascending ids)
+    want = np.sort(np.concatenate([gb["topk_idx"] + m * c.E for m in range(M)], axis=1), axis=1)
+    np.testing.assert_array_equal(gx["topk_idx"], want)
+    # outputs: expanded GPU vs base GPU over all tokens, and vs the fp64 base layer
+    r = rel_l2(gx["out"], gb["out"])
+    assert r <= 5e-3 and np.abs(gx["out"] - gb["out"]).max() <= 1e-2 * np.abs(gb["out"]).max()
+    tok = sample_tokens(L.T, 128, 30 + M)
+    ow = oracle_weights(L, st)
+    h64 = oracle.widen(L.h, "bf16")
+    s = oracle.router_logits(h64, ow.w_router, ow.b_router)
+    near = oracle.topk_gap(s, c.k) < 1e-5
+    tok = tok[~near[tok]]
+    ref = oracle.moe_forward(h64, ow, c.k, tokens=tok, workers=workers())
+    check_out(gx["out"][tok], ref["out"], "bf16")
+    print({"M": M, "gpu_vs_gpu_rel_l2": r})
+
+
+def test_random_64a8_prefill_4096_sampled():
+    L, st = layer_full(3)
+    m, _ = check_layer(L, st, tokens=sample_tokens(L.T, 128, 3))
+    print(m)
+
+
+def test_gpt_oss_120b_mxfp4_skewed_8192_sampled():
+    L, st = layer_full(4)
+    m, g = check_layer(L, st, tokens=sample_tokens(L.T, 128, 4))
+    counts = np.diff(g["expert_offsets"])
+    hot = counts[L.hot_set].sum() / counts.sum()
+    assert 0.49 <= hot <= 0.51
+    print(m, {"hot_share": float(hot)})
+
+
+def test_220a20b_mxfp4_prefill_2048_sampled():
+    L, st = layer_full(5)
+    m, _ = check_layer(L, st, tokens=sample_tokens(L.T, 48, 5))
+    print(m)
+
+
+def test_220a20b_mxfp4_decode_32_tokens():
+    L, st = layer_full(5)
+    m, _ = check_layer(with_T(L, 32), st)
+    print(m)
+
+
+# -------------------------------------------------------------- MXFP4 decode --
+
+def _bf16_bits_of(x64: np.ndarray) -> np.ndarray:
+    """bf16 bits of values that bf16 represents exactly (low half is zero)."""
+    b = x64.astype(np.float32).view(np.uint32)
+    assert not np.any(b[np.isfinite(x64)] & 0xFFFF)
+    return (b >> 16).astype(np.uint16)
+
+
+def test_mxfp4_decode_bit_exact_every_code_and_scale():
+    # every byte (two codes) with every scale 0..254: 16 groups of 16 bytes per scale
+    packed = np.tile(np.arange(256, dtype=np.uint8).reshape(16, 16), (255, 1))
+    scales = np.repeat(np.arange(255, dtype=np.uint8), 16)
+    ref = oracle.mxfp4_dequant(packed.reshape(-1, 16), scales.reshape(-1, 1))
+    out = torch.empty(packed.size * 2, dtype=torch.int16, device="cuda")
+    smoe.moe_mxfp4_decode(to_dev(packed, "u8"), to_dev(scales, "u8"), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16).reshape(ref.shape)
+    finite = np.abs(ref) <= float.fromhex("0x1.fep127")   # bf16 max
+    np.testing.assert_array_equal(got[finite], _bf16_bits_of(ref[finite]))
+    over = ~finite
+    assert np.all((got[over] & 0x7FFF) == 0x7F80)        # beyond bf16 range: +-inf
+    assert np.all((got[over] >> 15) == (ref[over] < 0))
+
+
+def test_mxfp4_decode_bit_exact_workload_weights():
+    L, st = layer_full(4)
+    for n in ("gate", "down"):
+        packed, scales = st[n][5], st["s_" + n][5]
+        ref = oracle.mxfp4_dequant(packed, scales)
+        out = torch.empty(ref.size, dtype=torch.int16, device="cuda")
+        smoe.moe_mxfp4_decode(to_dev(packed, "u8"), to_dev(scales, "u8"), out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(out.cpu().numpy().view(np.uint16), _bf16_bits_of(ref).ravel())
+
+
+# ---------------------------------------------------------------- interface --
+
+def test_zero_tokens_is_a_noop_and_errors_leave_outputs_untouched():
+    L, st = layer_full(1)
+    w = device_weights(L, st)
+    prob0 = problem(L.cfg, 0)
+    out = torch.full((4, 64), 7.0, device="cuda")
+    smoe.moe_forward(prob0, w, None, None, workspace=torch.empty(1, dtype=torch.uint8, device="cuda"),
+                     workspace_bytes=0)
+    prob = problem(L.cfg, 4)
+    h = to_dev(L.h[:4], "f32")
+    need = smoe.moe_workspace_bytes(prob)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(smoe.MoeError) as ei:
+        smoe.moe_forward(prob, w, h, out, workspace=ws, workspace_bytes=need - 1)
+    assert ei.value.status == -4
+    with pytest.raises(smoe.MoeError) as ei:
+        smoe.moe_forward(prob, w, h.view(-1)[1:].data_ptr(), out, workspace=ws)
+    assert ei.value.status == -5
+    bad = dataclasses.replace(prob, k=5)
+    with pytest.raises(smoe.MoeError) as ei:
+        smoe.moe_forward(bad, w, h, out, workspace=ws)
+    assert ei.value.status == -2
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_profile_hooks_report_every_stage():
+    L, st = layer_full(1)
+    prob = problem(L.cfg, 64)
+    w = device_weights(L, st)
+    h = to_dev(L.h, "f32")
+    out = torch.empty((64, 64), device="cuda")
+    smoe.moe_profile_begin(3)
+    for _ in range(5):
+        smoe.moe_forward(prob, w, h, out)
+    ms, calls = smoe.moe_profile_end()
+    assert calls == 3 and len(ms) == 5 and all(x > 0 for x in ms)
+    with pytest.raises(smoe.MoeError):
+        smoe.moe_profile_end()
