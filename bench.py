@@ -1,0 +1,202 @@
+"""Throughput of the sparse MoE feed-forward layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: the gpt-oss-20b MoE layer at prefill, T = 4,096 tokens, hidden 2,880,
+intermediate 2,880, 32 experts, top-4, bf16 activations and weights, fp32
+accumulation; seeded synthetic inputs (``synth``), resident in HBM before the
+timed region.  A step is one whole forward pass of the layer (router + top-k +
+softmax, routing permutation, gate/up GEMM with SiLU*up, down GEMM with the
+routing weight, combine), from h to out.
+
+Prints one JSON line: tokens/s over the timed steps, the whole layer's
+TFLOP/s and fraction of the bf16 MFMA peak, per-stage times from HIP events
+recorded on the launch stream during the timed steps, the roofline of the
+dominant kernel (the gate/up grouped GEMM), a decode measurement (T = 64, the
+first 64 rows) against the HBM roofline, and the fp64 CPU reference timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (prefill), % HBM GB/s (decode)"
+DOMINANT_STAGE = 2          # gate/up grouped GEMM
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_c2_prefill_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    return ap.parse_args()
+
+
+def layer_flops(T, H, I, E, k):
+    return 2.0 * T * E * H + 6.0 * T * k * H * I
+
+
+def gateup_flops(T, H, I, k):
+    return 4.0 * T * k * H * I
+
+
+def weight_bytes_touched(counts, H, I, elem_bytes):
+    return int((counts > 0).sum()) * 3 * H * I * elem_bytes
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    counter summary, valid only while the kernel source is unchanged."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        src = os.path.join(ROOT, "sparse_mixture_experts_token_amd", "csrc", "grouped_gemm.hip")
+        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != digest:
+            return None
+        return rec.get("hbm_bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(key, T_sample):
+    """The fp64 reference as it stands, on the first T_sample tokens."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    L = synth.make_layer(key, T=T_sample)
+    c = L.cfg
+    w = oracle.LayerWeights.from_storage(c.act, c.expert, L.w_router, L.b_router, L.expert)
+    h = oracle.widen(L.h, c.act)
+    t0 = time.perf_counter()
+    oracle.moe_forward(h, w, c.k)
+    dt = time.perf_counter() - t0
+    return {"value": T_sample / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {T_sample} of the {c.T} prefill tokens, whole layer in fp64 (NumPy), "
+                      f"expert weights generated and widened on the fly; {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import sparse_mixture_experts_token_amd as smoe
+    import synth
+
+    key = 2
+    c = synth.CONFIGS[key]
+    L = synth.make_layer(key)
+    st = L.stacked()
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    w = {"w_router": bf16(L.w_router), "b_router": bf16(L.b_router), "w_gate": bf16(st["gate"]),
+         "w_up": bf16(st["up"]), "w_down": bf16(st["down"])}
+    del st
+    h = bf16(L.h)
+    T, H, I, E, k = c.T, c.H, c.I, c.E, c.k
+    prob = smoe.Problem(T, H, I, E, k, smoe.MOE_BF16, smoe.MOE_BF16)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws_bytes = smoe.moe_workspace_bytes(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    routing = {"expert_offsets": offsets}
+
+    def step():
+        smoe.moe_forward(prob, w, h, out, routing=routing, workspace=ws, workspace_bytes=ws_bytes)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    smoe.moe_profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    stage_ms, calls = smoe.moe_profile_end()
+    ms_step = dt * 1e3 / args.steps
+    stage_avg = [x / calls for x in stage_ms]
+    F = layer_flops(T, H, I, E, k)
+    tok_s = T / (dt / args.steps)
+
+    g_ms = stage_avg[DOMINANT_STAGE]
+    g_tflops = gateup_flops(T, H, I, k) / (g_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
+                "kernel": "gateup_swiglu_gemm", "flops_per_launch": gateup_flops(T, H, I, k),
+                "avg_launch_ms": round(g_ms, 5)}
+
+    # ---- decode: first 64 tokens, HBM roofline on the touched experts' weights ----
+    Td = c.T_decode
+    pd = smoe.Problem(Td, H, I, E, k, smoe.MOE_BF16, smoe.MOE_BF16)
+    hd = h[:Td].contiguous()
+    outd = torch.empty((Td, H), dtype=torch.bfloat16, device=dev)
+    wsd_bytes = smoe.moe_workspace_bytes(pd)
+    wsd = torch.empty(wsd_bytes, dtype=torch.uint8, device=dev)
+    offd = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    for _ in range(10):
+        smoe.moe_forward(pd, w, hd, outd, routing={"expert_offsets": offd}, workspace=wsd, workspace_bytes=wsd_bytes)
+    torch.cuda.synchronize()
+    smoe.moe_profile_begin(args.decode_steps)
+    t1 = time.perf_counter()
+    for _ in range(args.decode_steps):
+        smoe.moe_forward(pd, w, hd, outd, routing={"expert_offsets": offd}, workspace=wsd, workspace_bytes=wsd_bytes)
+    torch.cuda.synchronize()
+    ddt = (time.perf_counter() - t1) / args.decode_steps
+    dstage, dcalls = smoe.moe_profile_end()
+    counts_d = np.diff(offd.cpu().numpy())
+    Bd = weight_bytes_touched(counts_d, H, I, 2) + E * H * 2 + E * 2 + 2 * Td * H * 2
+    decode = {"workload": f"first {Td} tokens, same layer", "tokens_per_s": round(Td / ddt, 1),
+              "ms_per_step": round(ddt * 1e3, 4), "alg_bytes": Bd, "hbm_GBps": round(Bd / ddt / 1e9, 1),
+              "hbm_frac": round(Bd / ddt / 1e9 / PEAK_HBM_GBPS, 4),
+              "stage_ms": [round(x / dcalls, 5) for x in dstage]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(key, args.cpu_sample_tokens)
+
+    res = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gpt-oss-20b MoE layer prefill, T=4096, hidden 2880, intermediate 2880, "
+                               "32 experts, top-4, bf16, fp32 accumulate", "T": T, "hidden": H,
+                   "intermediate": I, "experts": E, "top_k": k},
+        "layer_tflops": round(F / (ms_step * 1e-3) / 1e12, 2),
+        "layer_mfma_frac": round(F / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "stage_ms": {smoe.moe_stage_name(i): round(x, 5) for i, x in enumerate(stage_avg)},
+        "roofline": roofline, "decode": decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

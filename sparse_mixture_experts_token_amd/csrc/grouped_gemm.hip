@@ -1,5 +1,6 @@
-// Stages 2 and 3 of the layer: the experts' SwiGLU networks as two grouped
-// GEMMs over the expert-major row tiles ("gpt-oss 20B" field guide, cutaway 03:
+// Stages 2 and 3 of the layer for fp32 activations and weights (the generic
+// path; bf16 activations use the tuned kernels of gemm_prefill.hip): the
+// experts' SwiGLU networks as two grouped GEMMs over the expert-major row tiles ("gpt-oss 20B" field guide, cutaway 03:
 // SwiGLU experts; "openai/gpt-oss-20b" fixture comparison: hidden_act silu).
 //
 //   gate/up:  act[r, :] = silu(x_r W_gate[e]^T) * (x_r W_up[e]^T)
@@ -325,20 +326,21 @@ Args make_args(const GemmProblem& p, int mode) {
 
 }  // namespace
 
-int gemm_block_m(int, int, int, int, int) { return kBM; }
+int prefill_block_m();
+hipError_t launch_gateup_bf16(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_down_bf16(const GemmProblem& p, hipStream_t stream);
 
+int gemm_block_m(int act_dtype, int, int, int, int) { return act_dtype == DT_F32 ? kBM : prefill_block_m(); }
+
+// fp32 activations take the generic kernel; bf16 activations the tuned one.
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream) {
-    Args a = make_args(p, 0);
-    if (p.act_dtype == DT_F32) return launch_on<0, float, DT_F32, kBM, kBNGateUp>(a, stream);
-    if (p.expert_dtype == DT_MXFP4) return launch_on<0, uint16_t, DT_MXFP4, kBM, kBNGateUp>(a, stream);
-    return launch_on<0, uint16_t, DT_BF16, kBM, kBNGateUp>(a, stream);
+    if (p.act_dtype == DT_F32) return launch_on<0, float, DT_F32, kBM, kBNGateUp>(make_args(p, 0), stream);
+    return launch_gateup_bf16(p, stream);
 }
 
 hipError_t launch_down(const GemmProblem& p, hipStream_t stream) {
-    Args a = make_args(p, 1);
-    if (p.act_dtype == DT_F32) return launch_on<1, float, DT_F32, kBM, kBNDown>(a, stream);
-    if (p.expert_dtype == DT_MXFP4) return launch_on<1, uint16_t, DT_MXFP4, kBM, kBNDown>(a, stream);
-    return launch_on<1, uint16_t, DT_BF16, kBM, kBNDown>(a, stream);
+    if (p.act_dtype == DT_F32) return launch_on<1, float, DT_F32, kBM, kBNDown>(make_args(p, 1), stream);
+    return launch_down_bf16(p, stream);
 }
 
 }  // namespace moe

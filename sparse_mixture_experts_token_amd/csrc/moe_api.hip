@@ -26,6 +26,7 @@ int check_problem(const moe_problem* p) {
     if (p->H % 64 != 0 || p->I % 64 != 0) return MOE_ERR_SHAPE;
     const int64_t big = (int64_t)p->T * p->k * (p->H > p->I ? p->H : p->I);
     if (big >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
+    if ((int64_t)p->H * p->I >= (int64_t(1) << 29)) return MOE_ERR_SHAPE;
     const bool ok = (p->act_dtype == MOE_F32 && p->expert_dtype == MOE_F32) ||
                     (p->act_dtype == MOE_BF16 && (p->expert_dtype == MOE_BF16 || p->expert_dtype == MOE_MXFP4));
     if (!ok) return MOE_ERR_DTYPE;

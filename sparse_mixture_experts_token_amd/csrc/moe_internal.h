@@ -13,6 +13,10 @@ namespace moe {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+// Native 4 x u32 vector.  Arrays of HIP's uint4 (a struct wrapping a union)
+// are left in scratch memory by the compiler; arrays of this type are kept in
+// registers.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 enum : int { DT_F32 = 0, DT_BF16 = 1, DT_MXFP4 = 2 };
 
@@ -26,6 +30,23 @@ struct Tile {
     int32_t rows;       // valid rows, 1..BM
     int32_t pad;
 };
+
+// ------------------------------------------------------------ buffer loads --
+// Raw buffer loads: a 128-bit descriptor (base, size in bytes) in scalar
+// registers plus a 32-bit per-lane byte offset and a scalar byte offset.  No
+// 64-bit per-lane address arithmetic, and reads at or beyond `bytes` return 0.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+constexpr int kBufDword3 = 0x00020000;  // gfx9-family raw buffer: no format conversion
+
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufDword3);
+}
+__device__ __forceinline__ u32x4 buf_load16(buf_rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load1(buf_rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
 
 // ------------------------------------------------------ bf16 conversions --
 
@@ -77,7 +98,7 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_bf16x2(uint32_t w, float sc, int b
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ void decode_mxfp4_32(const uint4& q, uint32_t scale, uint32_t out[16]) {
+__device__ __forceinline__ void decode_mxfp4_32(const u32x4& q, uint32_t scale, uint32_t out[16]) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     if (scale >= 2u && scale <= 252u) {
         const float sc = __uint_as_float(scale << 23);  // 2^(scale-127), a normal float

@@ -7,15 +7,15 @@
 
 namespace {
 
-__global__ __launch_bounds__(256) void mxfp4_decode_kernel(const uint4* __restrict__ packed,
+__global__ __launch_bounds__(256) void mxfp4_decode_kernel(const moe::u32x4* __restrict__ packed,
                                                            const uint8_t* __restrict__ scales, int64_t groups,
-                                                           uint4* __restrict__ out) {
+                                                           moe::u32x4* __restrict__ out) {
     for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
          g += (int64_t)gridDim.x * blockDim.x) {
         uint32_t d[16];
         moe::decode_mxfp4_32(packed[g], scales[g], d);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[g * 4 + i] = uint4{d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]};
+        for (int i = 0; i < 4; ++i) out[g * 4 + i] = moe::u32x4{d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]};
     }
 }
 
@@ -30,6 +30,6 @@ extern "C" int moe_mxfp4_decode(const uint8_t* packed, const uint8_t* scales, in
     const int64_t blocks64 = (n_groups + 255) / 256;
     const int blocks = (int)(blocks64 < 16384 ? blocks64 : 16384);
     mxfp4_decode_kernel<<<blocks, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
-        reinterpret_cast<const uint4*>(packed), scales, n_groups, reinterpret_cast<uint4*>(out_bf16));
+        reinterpret_cast<const moe::u32x4*>(packed), scales, n_groups, reinterpret_cast<moe::u32x4*>(out_bf16));
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
