@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -66,7 +68,7 @@ def measured_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        src = os.path.join(ROOT, "sparse_mixture_experts_token_amd", "csrc", "grouped_gemm.hip")
+        src = os.path.join(ROOT, "sparse_mixture_experts_token_amd", "csrc", "gemm_prefill.hip")
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
         if rec.get("source_sha256") != digest:
             return None
@@ -106,6 +108,16 @@ def main():
     import torch
     import sparse_mixture_experts_token_amd as smoe
     import synth
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        a = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}))
+        return
 
     key = 2
     c = synth.CONFIGS[key]

@@ -6,36 +6,51 @@
 //   gate/up:  act[r, :] = silu(x_r W_gate[e]^T) * (x_r W_up[e]^T),  x_r = h[token of row r]
 //   down:     y[a, :]   = p_a * (act[r, :] W_down[e]^T),            a = perm_src[r]
 //
-// Workgroup tile: BM = 128 rows of one expert x BN weight rows (per matrix),
-// K swept in steps of 64 through two LDS stages.  The four waves split N
-// (1 x 4): every wave owns all 128 rows and BN/4 columns of each matrix, as
-// 16x16x32 bf16 MFMA tiles with fp32 accumulators (gate/up: 8 x 3 tiles of
-// gate and of up = 192 accumulators; down: 8 x 5 tiles = 160).  BN = 192
-// (gate/up) and 320 (down) divide 2880 exactly.
+// Workgroup tile: BM = 256 rows of one expert x BN weight rows per matrix,
+// eight waves in a 4 x 2 layout (two waves per SIMD).  Wave (wm, wn) owns the
+// 32-row blocks wm and wm + 4 (interleaved, so a short row tile still splits
+// evenly) and columns wn*BN/2 .. (wn+1)*BN/2 of every matrix, as 32x32x16
+// bf16 MFMA tiles with fp32 accumulators (gate/up: 2 x 3 tiles of gate and
+// the matching 2 x 3 of up = 192 accumulators, so SiLU*up is formed in
+// registers; down: 2 x 5 = 160).  BN = 192 (gate/up) and 320 (down) divide
+// 2880 exactly.  From one wave the 32x32x16 form issues at about twice the
+// rate of the 16x16x32 form on this hardware; 256-row tiles halve the weight
+// traffic of 128-row ones.
 //
-// LDS rows are 128 bytes (64 bf16 of K); the 16-byte chunk c of row r is
-// stored at chunk c ^ (r & 7) ^ ((r >> 3) & 1).  Fragment reads (16 rows, one
-// chunk) then hit distinct banks whether the LDS serves 8 lanes per cycle
-// (rows r..r+7 take all 8 chunk slots) or 16 (rows r and r+8 differ too), and
-// the staging writes (whole rows) are conflict-free as well.
+// K is swept 32 at a time through a ring of 3 LDS stages filled by
+// buffer-to-LDS DMA loads (no staging registers), two stages in flight.
+// A stage holds every operand fragment as one 1 KB block in fragment order:
+// for K half s of the stage, lane l of the 32x32x16 MFMA reads bytes
+// 16l..16l+15 of its block, i.e. row (or weight column) l mod 32 and K
+// elements 16s + 8(l/32) .. +7.  Fragment reads are thus linear
+// (conflict-free), and each DMA instruction writes one block linearly while
+// its lanes fetch the matching rows from memory.
 //
-// MXFP4 weights are decoded exactly to bf16 while being staged into LDS.
-// Row tiles shorter than 128 rows run only the first 4, 2 or 1 16-row blocks
-// when the rest are empty (separate branch-free loop instantiations).
+// MXFP4 weights are staged packed (fragment order in 4-byte slots, 256-byte
+// blocks) with the tile's scales for all of K, and decoded exactly to bf16 in
+// registers right before the MFMAs.
+//
+// A wave whose 32-row blocks are empty skips their MFMAs (branch-free loop
+// instantiations for 2, 1 or 0 live blocks; all take the same barriers).
+// Every wave issues the same number of DMA loads per stage (padded with loads
+// into a scratch block), so one vmcnt threshold serves all of them.
 //
 // Block order: each XCD (blocks are dealt round-robin to 8) gets a contiguous
-// range of the (row tile, column tile) space; inside it, GROUP_M row tiles are
-// swept across all column tiles, so a weight tile is fetched once per group
-// and the group's activation rows stay in that XCD's L2.
+// range of a work list built with the routing tables: experts in order, for
+// each expert its column tiles, for each column tile all the expert's row
+// tiles.  An expert's row tiles then read each weight tile at about the same
+// time on one XCD (one fetch from HBM, the rest from L2), and its activation
+// rows stay in that XCD's L2 across the column tiles.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBM = 128;
-constexpr int kBK = 64;
-constexpr int kGroupM = 4;
+constexpr int kThreads = 512;
+constexpr int kWaves = 8;
+constexpr int kBM = 256;
+constexpr int kBK = 32;      // K per LDS stage
+constexpr int kStages = 3;   // LDS ring depth (two stages in flight)
 constexpr int kXcds = 8;
 constexpr int kBNGateUp = 192;
 constexpr int kBNDown = 320;
@@ -49,154 +64,163 @@ struct PArgs {
     const int32_t* perm_src;
     const float* topk_w;
     const Tile* tiles;
-    const int32_t* n_tiles;
+    const int32_t* work;     // row tile * n_ntiles + column tile, expert-grouped order
+    const int32_t* n_work;
     void* out;
-    uint32_t a_bytes;       // size of the activation buffer
-    int max_tiles, n_ntiles;
+    uint32_t a_bytes;        // size of the activation buffer
+    int max_work, n_ntiles;
     int K, N, k;
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-    return (row << 7) + (((chunk ^ row ^ (row >> 3)) & 7) << 4);
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer-to-LDS DMA: lane l's `bytes` land at lds_block + bytes * l.
+__device__ __forceinline__ void dma16(buf_rsrc r, unsigned char* lds_block, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(buf_rsrc r, unsigned char* lds_block, uint32_t voff, uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_block, 4, voff, soff, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    else static_assert(N == 0, "add the count");
+}
+
+// Workgroup barrier without the release fence of __syncthreads(): that fence
+// would wait for every DMA load in flight (they count as LDS writes).  Callers
+// wait for exactly the loads they need first; the empty asm statements keep
+// the compiler from moving memory accesses across the barrier.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
 template <int MODE, int WDT, int BN>
 struct PCfg {
+    static constexpr bool MX = WDT == DT_MXFP4;
     static constexpr int NMAT = MODE == 0 ? 2 : 1;
-    static constexpr int WN = BN / 4;             // columns per wave per matrix
-    static constexpr int NBW = WN / 16;           // 16-col blocks per wave per matrix
-    static constexpr int MBW = kBM / 16;          // 16-row blocks
-    static constexpr int BROWS = NMAT * BN;       // weight rows per stage
-    static constexpr int A_CH = kBM * 8 / kThreads;                 // 16B chunks of A per thread
-    static constexpr int PER_ROW = WDT == DT_MXFP4 ? 2 : 8;         // 16B chunks per weight row per stage
-    static constexpr int M_CH_TOTAL = BN * PER_ROW;                 // chunks of one matrix per stage
-    static constexpr int M_CH = (M_CH_TOTAL + kThreads - 1) / kThreads;  // per thread per matrix
-    static constexpr int B_CH = NMAT * M_CH;
-    static constexpr int STAGE = (kBM + BROWS) * 128;               // bytes per LDS stage
-    static constexpr size_t SMEM = 2 * (size_t)STAGE;
-    static_assert(BN % 64 == 0, "BN");
+    static constexpr int MBW = 2;                     // 32-row blocks per wave
+    static constexpr int BPM = BN / 32;               // 32-column blocks per matrix
+    static constexpr int NBW = BPM / 2;               // 32-column blocks per wave per matrix
+    static constexpr int A_BLK = (kBM / 32) * 2;      // activation blocks per stage (row blocks x 2 K halves)
+    static constexpr int B_BLK = NMAT * BPM * 2;      // weight blocks per stage
+    static constexpr int A_DMA = A_BLK / kWaves;      // issued per wave per stage
+    static constexpr int B_DMA = (B_BLK + kWaves - 1) / kWaves;
+    static constexpr int BBLK = MX ? 256 : 1024;      // bytes per weight block
+    static constexpr int A_BYTES = A_BLK * 1024;
+    static constexpr int STAGE = A_BYTES + B_BLK * BBLK;
+    static constexpr int PAD_OFF = kStages * STAGE;   // scratch block for padding DMA loads
+    static constexpr int PAD_BYTES = (B_BLK % kWaves) ? 1024 : 0;
+    static constexpr int SCALE_OFF = PAD_OFF + PAD_BYTES;
+    static constexpr int DMA_PER_STAGE = A_DMA + B_DMA;  // per thread
+    static_assert(A_BLK % kWaves == 0, "activation blocks must split evenly over the waves");
+    static_assert(BPM % 2 == 0, "columns must split over two waves");
 };
-
-// Chunk j of a thread belongs to matrix j / M_CH (uniform across the
-// workgroup, so the weight base stays scalar) and is chunk
-// tid + 256 * (j % M_CH) of that matrix's stage tile.
-template <class C>
-__device__ __forceinline__ bool chunk_live(int tid, int j) {
-    return C::M_CH_TOTAL % kThreads == 0 || tid + kThreads * (j % C::M_CH) < C::M_CH_TOTAL;
-}
 
 struct Srcs {
-    buf_rsrc a;      // activations (h or act)
-    buf_rsrc w[2];   // this expert's gate/up (or down) matrix
-    buf_rsrc s[2];   // MXFP4 scales of those matrices
+    buf_rsrc a;     // activations
+    buf_rsrc w[2];  // this expert's matrices
+    buf_rsrc s[2];  // MXFP4 scales of those matrices
 };
 
-template <class C, int WDT>
-__device__ __forceinline__ void load_stage(const Srcs& src, const uint32_t (&a_off)[C::A_CH],
-                                           const uint32_t (&b_off)[C::B_CH], const uint32_t (&s_off)[C::B_CH],
-                                           int k0, u32x4 (&ra)[C::A_CH], u32x4 (&rb)[C::B_CH],
-                                           uint32_t (&rs)[C::B_CH]) {
+// Weight block b = wave + 8i (over both matrices; b >= B_BLK is a padding load).
+template <class C>
+__device__ __forceinline__ void dma_stage(const Srcs& src, unsigned char* smem, int kt, int wave,
+                                          const uint32_t (&a_voff)[C::A_DMA], const uint32_t (&b_voff)[C::B_DMA],
+                                          const int (&b_mat)[C::B_DMA]) {
+    unsigned char* st = smem + (kt % kStages) * C::STAGE;
+    const uint32_t k0 = (uint32_t)kt * kBK;
 #pragma unroll
-    for (int j = 0; j < C::A_CH; ++j) ra[j] = buf_load16(src.a, a_off[j], (uint32_t)k0 * 2);
+    for (int i = 0; i < C::A_DMA; ++i) dma16(src.a, st + (wave + kWaves * i) * 1024, a_voff[i], k0 * 2);
 #pragma unroll
-    for (int j = 0; j < C::B_CH; ++j) {
-        const int m = j / C::M_CH;
-        if constexpr (WDT == DT_MXFP4) {
-            rb[j] = buf_load16(src.w[m], b_off[j], (uint32_t)k0 / 2);
-            rs[j] = buf_load1(src.s[m], s_off[j], (uint32_t)k0 / 32);
+    for (int i = 0; i < C::B_DMA; ++i) {
+        const int b = wave + kWaves * i;
+        unsigned char* blk = b < C::B_BLK ? st + C::A_BYTES + b * C::BBLK : smem + C::PAD_OFF;
+        const buf_rsrc r = b_mat[i] ? src.w[1] : src.w[0];
+        if constexpr (C::MX) dma4(r, blk, b_voff[i], k0 / 2);
+        else dma16(r, blk, b_voff[i], k0 * 2);
+    }
+}
+
+// Weight operand of block (m, cb, s) for this lane.
+template <class C>
+__device__ __forceinline__ bf16x8 w_frag(const unsigned char* st, const unsigned char* scales, int kg, int kt,
+                                         int m, int cb, int s, int lane, int BN) {
+    const int blk = (m * C::BPM + cb) * 2 + s;
+    if constexpr (C::MX) {
+        const uint32_t q = *reinterpret_cast<const uint32_t*>(st + C::A_BYTES + blk * C::BBLK + lane * 4);
+        const uint32_t scale = scales[(m * BN + cb * 32 + (lane & 31)) * kg + kt];
+        u32x4 v;
+        if (scale >= 2u && scale <= 252u) {
+            const float sc = __uint_as_float(scale << 23);
+            v = u32x4{cvt_fp4x2_bf16x2(q, sc, 0), cvt_fp4x2_bf16x2(q, sc, 1), cvt_fp4x2_bf16x2(q, sc, 2),
+                      cvt_fp4x2_bf16x2(q, sc, 3)};
         } else {
-            rb[j] = buf_load16(src.w[m], b_off[j], (uint32_t)k0 * 2);
+            uint32_t w[4];
+#pragma unroll
+            for (int bb = 0; bb < 4; ++bb) {
+                const uint32_t byte = (q >> (8 * bb)) & 0xffu;
+                w[bb] = e2m1_to_bf16_exact(byte & 0xfu, scale) | (e2m1_to_bf16_exact(byte >> 4, scale) << 16);
+            }
+            v = u32x4{w[0], w[1], w[2], w[3]};
         }
+        return __builtin_bit_cast(bf16x8, v);
+    } else {
+        return *reinterpret_cast<const bf16x8*>(st + C::A_BYTES + blk * C::BBLK + lane * 16);
     }
 }
 
-template <class C, int WDT, int BN>
-__device__ __forceinline__ void store_stage(unsigned char* stage, int tid, const u32x4 (&ra)[C::A_CH],
-                                            const u32x4 (&rb)[C::B_CH], const uint32_t (&rs)[C::B_CH]) {
-    unsigned char* sbt = stage + kBM * 128;
-#pragma unroll
-    for (int j = 0; j < C::A_CH; ++j) {
-        const int c = tid + kThreads * j;
-        *reinterpret_cast<u32x4*>(stage + swz(c >> 3, c & 7)) = ra[j];
-    }
-#pragma unroll
-    for (int j = 0; j < C::B_CH; ++j) {
-        if (!chunk_live<C>(tid, j)) continue;
-        const int m = j / C::M_CH;
-        const int c = tid + kThreads * (j % C::M_CH);
-        if constexpr (WDT == DT_MXFP4) {
-            const int r = m * BN + (c >> 1), gq = c & 1;
-            uint32_t d[16];
-            decode_mxfp4_32(rb[j], rs[j], d);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *reinterpret_cast<u32x4*>(sbt + swz(r, gq * 4 + i)) = u32x4{d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]};
-        } else {
-            *reinterpret_cast<u32x4*>(sbt + swz(m * BN + (c >> 3), c & 7)) = rb[j];
-        }
-    }
-}
-
-// Fragments of one 64-deep K step (both 32-wide halves) of this wave.
+// The MFMAs of one 32-deep stage for this wave's MB live 32-row blocks,
+// one 16-deep half at a time (fragments of a half are read, then used).
 template <class C, int BN, int MB>
-struct Frags {
-    bf16x8 a[2][MB];
-    bf16x8 b[2][C::NMAT][C::NBW];
-};
-
-template <class C, int BN, int MB>
-__device__ __forceinline__ void read_frags(const unsigned char* stage, int wave, int lane, Frags<C, BN, MB>& f) {
-    const unsigned char* sbt = stage + kBM * 128;
-    const int fr = lane & 15;
-    const int fq = lane >> 4;
+__device__ __forceinline__ void mma_stage(const unsigned char* st, const unsigned char* scales, int kg, int kt,
+                                          int wm, int wn, int lane, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+    if constexpr (MB == 0) {
+        return;
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int chunk = ks * 4 + fq;
+        for (int s = 0; s < 2; ++s) {
+            bf16x8 af[MB];
+            bf16x8 bfr[C::NMAT][C::NBW];
 #pragma unroll
-        for (int m = 0; m < C::NMAT; ++m)
-#pragma unroll
-            for (int j = 0; j < C::NBW; ++j)
-                f.b[ks][m][j] = *reinterpret_cast<const bf16x8*>(sbt + swz(m * BN + wave * C::WN + j * 16 + fr, chunk));
-#pragma unroll
-        for (int i = 0; i < MB; ++i) f.a[ks][i] = *reinterpret_cast<const bf16x8*>(stage + swz(i * 16 + fr, chunk));
-    }
-}
-
-template <class C, int BN, int MB>
-__device__ __forceinline__ void mfma_frags(const Frags<C, BN, MB>& f, f32x4 (&acc)[C::NMAT][C::MBW][C::NBW]) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
+            for (int i = 0; i < MB; ++i)
+                af[i] = *reinterpret_cast<const bf16x8*>(st + ((wm + 4 * i) * 2 + s) * 1024 + lane * 16);
 #pragma unroll
             for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
-                for (int j = 0; j < C::NBW; ++j) acc[m][i][j] = mfma16(f.a[ks][i], f.b[ks][m][j], acc[m][i][j]);
+                for (int j = 0; j < C::NBW; ++j) bfr[m][j] = w_frag<C>(st, scales, kg, kt, m, wn * C::NBW + j, s, lane, BN);
+#pragma unroll
+            for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+                for (int j = 0; j < C::NBW; ++j)
+#pragma unroll
+                    for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(af[i], bfr[m][j], acc[m][i][j]);
+        }
+    }
 }
 
-template <class C, int WDT, int BN, int MB>
-__device__ __forceinline__ void main_loop(const Srcs& src, unsigned char* smem, int nk,
-                                          const uint32_t (&a_off)[C::A_CH], const uint32_t (&b_off)[C::B_CH],
-                                          const uint32_t (&s_off)[C::B_CH], u32x4 (&ra)[C::A_CH],
-                                          u32x4 (&rb)[C::B_CH], uint32_t (&rs)[C::B_CH],
-                                          f32x4 (&acc)[C::NMAT][C::MBW][C::NBW]) {
-    const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+template <class C, int BN, int MB>
+__device__ __forceinline__ void main_loop(const Srcs& src, unsigned char* smem, const unsigned char* scales, int nk,
+                                          int wave, int lane, const uint32_t (&a_voff)[C::A_DMA],
+                                          const uint32_t (&b_voff)[C::B_DMA], const int (&b_mat)[C::B_DMA],
+                                          f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+    const int wm = wave >> 1, wn = wave & 1;
     for (int kt = 0; kt < nk; ++kt) {
-        const int buf = kt & 1;
-        // Order within a K step: this stage's fragment reads, then the next
-        // stage's global loads, then the MFMAs (fences keep the compiler from
-        // interleaving them, which made the fragment reads wait on the loads).
-        Frags<C, BN, MB> f;
-        read_frags<C, BN, MB>(smem + buf * C::STAGE, wave, lane, f);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < nk) load_stage<C, WDT>(src, a_off, b_off, s_off, (kt + 1) * kBK, ra, rb, rs);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_frags<C, BN, MB>(f, acc);
-        if (kt + 1 < nk) store_stage<C, WDT, BN>(smem + (buf ^ 1) * C::STAGE, tid, ra, rb, rs);
-        __syncthreads();
+        // stage kt landed for this thread (the next one may still be in flight) ...
+        if (kt + kStages - 2 < nk) wait_vmcnt<(kStages - 2) * C::DMA_PER_STAGE>();
+        else wait_vmcnt<0>();
+        // ... and for every thread; everyone is also done reading stage kt - 1
+        // (each wave waited for its fragment reads before its MFMAs).
+        bare_barrier();
+        if (kt + kStages - 1 < nk) dma_stage<C>(src, smem, kt + kStages - 1, wave, a_voff, b_voff, b_mat);
+        mma_stage<C, BN, MB>(smem + (kt % kStages) * C::STAGE, scales, nk, kt, wm, wn, lane, acc);
     }
 }
 
@@ -205,18 +229,13 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
     using C = PCfg<MODE, WDT, BN>;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    // ---- block -> (row tile, column tile) ----
-    const int nblocks = args.max_tiles * args.n_ntiles;
-    const int per_xcd = (nblocks + kXcds - 1) / kXcds;
+    // ---- block -> work item (row tile, column tile) ----
+    const int per_xcd = (args.max_work + kXcds - 1) / kXcds;
     const int q = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (q >= nblocks) return;
-    const int group_span = kGroupM * args.n_ntiles;
-    const int g = q / group_span;
-    const int in_g = q % group_span;
-    const int g_rows = min(kGroupM, args.max_tiles - g * kGroupM);
-    const int mt = g * kGroupM + in_g % g_rows;
-    const int nt = in_g / g_rows;
-    if (mt >= args.n_tiles[0]) return;
+    if (q >= args.max_work || q >= args.n_work[0]) return;
+    const int item = args.work[q];
+    const int mt = item / args.n_ntiles;
+    const int nt = item % args.n_ntiles;
     const Tile tile = args.tiles[mt];
     const int e = tile.expert;
     const int row0 = tile.row_start;
@@ -226,23 +245,27 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;   // 4 x 2 waves
+    const int fr = lane & 31;   // row / column within a 32-block
+    const int fh = lane >> 5;   // which 8 of the 16 K elements of a half
 
-    // ---- per-thread global sources: scalar bases + 32-bit offsets ----
-    uint32_t a_off[C::A_CH];  // elements
+    // ---- DMA sources (byte offsets) ----
+    // activation block b = wave + 8i: row block b / 2, K half b % 2
+    uint32_t a_voff[C::A_DMA];
 #pragma unroll
-    for (int j = 0; j < C::A_CH; ++j) {
-        const int c = tid + kThreads * j;
-        const int r = c >> 3;
+    for (int i = 0; i < C::A_DMA; ++i) {
+        const int b = wave + kWaves * i;
+        const int r = (b >> 1) * 32 + fr;
         const int rr = r < rows ? r : 0;
         int src_row;
         if constexpr (MODE == 0) src_row = args.perm_src[row0 + rr] / args.k;
         else src_row = row0 + rr;
-        a_off[j] = (uint32_t)(src_row * K + (c & 7) * 8) * 2u;
+        a_voff[i] = (uint32_t)(src_row * K + ((b & 1) * 2 + fh) * 8) * 2u;
     }
     const size_t mat_elems = (size_t)N * K;
     Srcs src;
     src.a = make_rsrc(args.a_src, args.a_bytes);
-    if constexpr (WDT == DT_MXFP4) {
+    if constexpr (C::MX) {
         const uint32_t wbytes = (uint32_t)(mat_elems / 2), sbytes = (uint32_t)(mat_elems / 32);
         src.w[0] = make_rsrc((const unsigned char*)args.w0 + (size_t)e * wbytes, wbytes);
         src.w[1] = MODE == 0 ? make_rsrc((const unsigned char*)args.w1 + (size_t)e * wbytes, wbytes) : src.w[0];
@@ -254,64 +277,71 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
         src.w[1] = MODE == 0 ? make_rsrc((const unsigned char*)args.w1 + (size_t)e * wbytes, wbytes) : src.w[0];
         src.s[0] = src.s[1] = src.w[0];
     }
-    uint32_t b_off[C::B_CH];  // bytes: row start + chunk (bf16) or group (mxfp4) at k = 0
-    uint32_t s_off[C::B_CH];  // mxfp4: scale index of the chunk's group at k = 0
+    // weight block b = wave + 8i over both matrices: matrix b / (2 BPM), then
+    // column block (b mod 2 BPM) / 2 and K half b mod 2; padding loads repeat block 0
+    uint32_t b_voff[C::B_DMA];
+    int b_mat[C::B_DMA];
 #pragma unroll
-    for (int j = 0; j < C::B_CH; ++j) {
-        const int c = min(tid + kThreads * (j % C::M_CH), C::M_CH_TOTAL - 1);
-        const int r = c / C::PER_ROW;
-        const int cc = c % C::PER_ROW;
-        const int n = min(n0 + r, N - 1);
-        if constexpr (WDT == DT_MXFP4) {
-            b_off[j] = (uint32_t)(n * (K / 2) + cc * 16);
-            s_off[j] = (uint32_t)(n * (K / 32) + cc);
-        } else {
-            b_off[j] = (uint32_t)(n * K * 2 + cc * 16);
-            s_off[j] = 0;
-        }
+    for (int i = 0; i < C::B_DMA; ++i) {
+        int b = wave + kWaves * i;
+        if (b >= C::B_BLK) b = 0;
+        b_mat[i] = b / (C::BPM * 2);
+        const int bm = b % (C::BPM * 2);
+        const int n = min(n0 + (bm >> 1) * 32 + fr, N - 1);
+        const int kc = (bm & 1) * 2 + fh;   // 8-element K chunk within the stage
+        if constexpr (C::MX) b_voff[i] = (uint32_t)(n * (K / 2) + kc * 4);
+        else b_voff[i] = (uint32_t)(n * K + kc * 8) * 2u;
     }
 
-    u32x4 ra[C::A_CH];
-    u32x4 rb[C::B_CH];
-    uint32_t rs[C::B_CH];
-    f32x4 acc[C::NMAT][C::MBW][C::NBW];
+    const int nk = K / kBK;
+    // prologue: the first kStages-1 stages in flight
+#pragma unroll
+    for (int s = 0; s < kStages - 1; ++s)
+        if (s < nk) dma_stage<C>(src, smem, s, wave, a_voff, b_voff, b_mat);
+
+    // MXFP4: this tile's scales for the whole K range, [matrix][column][K/32]
+    unsigned char* scales = smem + C::SCALE_OFF;
+    if constexpr (C::MX) {
+        const int kg = K / 32;
+        const int per_mat = BN * kg;  // bytes, a multiple of 16
+        for (int m = 0; m < C::NMAT; ++m)
+            for (int c = tid * 16; c < per_mat; c += kThreads * 16) {
+                const u32x4 v = buf_load16(src.s[m], (uint32_t)(n0 * kg + c), 0);
+                *reinterpret_cast<u32x4*>(scales + m * per_mat + c) = v;
+            }
+        __syncthreads();
+    }
+
+    f32x16 acc[C::NMAT][C::MBW][C::NBW];
 #pragma unroll
     for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
         for (int i = 0; i < C::MBW; ++i)
 #pragma unroll
-            for (int j = 0; j < C::NBW; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < C::NBW; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[m][i][j][v] = 0.f;
 
-    const int nk = K / kBK;
-    load_stage<C, WDT>(src, a_off, b_off, s_off, 0, ra, rb, rs);
-    store_stage<C, WDT, BN>(smem, tid, ra, rb, rs);
-    __syncthreads();
-    // Only the 16-row blocks that hold rows get MFMAs: 8, 4, 2 or 1 of them.
-    const int live = (rows + 15) >> 4;
-    if (live > 4)
-        main_loop<C, WDT, BN, 8>(src, smem, nk, a_off, b_off, s_off, ra, rb, rs, acc);
-    else if (live > 2)
-        main_loop<C, WDT, BN, 4>(src, smem, nk, a_off, b_off, s_off, ra, rb, rs, acc);
-    else if (live > 1)
-        main_loop<C, WDT, BN, 2>(src, smem, nk, a_off, b_off, s_off, ra, rb, rs, acc);
-    else
-        main_loop<C, WDT, BN, 1>(src, smem, nk, a_off, b_off, s_off, ra, rb, rs, acc);
+    // This wave's live 32-row blocks: wm and wm + 4 below ceil(rows / 32).
+    const int live32 = (rows + 31) >> 5;
+    const int mine = (wm < live32 ? 1 : 0) + (wm + 4 < live32 ? 1 : 0);
+    if (mine == 2) main_loop<C, BN, 2>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    else if (mine == 1) main_loop<C, BN, 1>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    else main_loop<C, BN, 0>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
 
-    const int fr = lane & 15;
-    const int fq = lane >> 4;
     // ---- epilogue ----
 #pragma unroll
     for (int i = 0; i < C::MBW; ++i) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int r = i * 16 + fq * 4 + jj;
+        for (int v = 0; v < 16; ++v) {
+            const int r = (wm + 4 * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
             if (r >= rows) continue;
             if constexpr (MODE == 0) {
                 uint16_t* orow = reinterpret_cast<uint16_t*>(args.out) + (size_t)(row0 + r) * N;
 #pragma unroll
                 for (int j = 0; j < C::NBW; ++j) {
-                    const int n = n0 + wave * C::WN + j * 16 + fr;
-                    if (n < N) orow[n] = (uint16_t)f32_to_bf16_bits(silu_f(acc[0][i][j][jj]) * acc[1][i][j][jj]);
+                    const int n = n0 + (wn * C::NBW + j) * 32 + fr;
+                    if (n < N) orow[n] = (uint16_t)f32_to_bf16_bits(silu_f(acc[0][i][j][v]) * acc[1][i][j][v]);
                 }
             } else {
                 const int asg = args.perm_src[row0 + r];
@@ -319,8 +349,8 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
                 float* orow = reinterpret_cast<float*>(args.out) + (size_t)asg * N;
 #pragma unroll
                 for (int j = 0; j < C::NBW; ++j) {
-                    const int n = n0 + wave * C::WN + j * 16 + fr;
-                    if (n < N) orow[n] = acc[0][i][j][jj] * p;
+                    const int n = n0 + (wn * C::NBW + j) * 32 + fr;
+                    if (n < N) orow[n] = acc[0][i][j][v] * p;
                 }
             }
         }
@@ -328,30 +358,32 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
 }
 
 template <int WDT>
-__global__ __launch_bounds__(kThreads, 1) void gateup_gemm_kernel(PArgs args) {
+__global__ __launch_bounds__(kThreads) void gateup_gemm_kernel(PArgs args) {
     gemm_body<0, WDT, kBNGateUp>(args);
 }
 
 template <int WDT>
-__global__ __launch_bounds__(kThreads, 1) void down_gemm_kernel(PArgs args) {
+__global__ __launch_bounds__(kThreads) void down_gemm_kernel(PArgs args) {
     gemm_body<1, WDT, kBNDown>(args);
+}
+
+template <int MODE, int WDT, int BN>
+size_t smem_bytes(int K) {
+    using C = PCfg<MODE, WDT, BN>;
+    return (size_t)C::SCALE_OFF + (C::MX ? (size_t)C::NMAT * BN * (K / 32) : 0);
 }
 
 template <typename Kern>
 hipError_t launch_k(Kern kern, size_t smem, const PArgs& a, hipStream_t stream) {
-    const int nblocks = a.max_tiles * a.n_ntiles;
-    const int per_xcd = (nblocks + kXcds - 1) / kXcds;
+    const int per_xcd = (a.max_work + kXcds - 1) / kXcds;
     kern<<<per_xcd * kXcds, kThreads, smem, stream>>>(a);
     return hipGetLastError();
 }
-
-PArgs make_pargs(const GemmProblem& p, int mode, int BN) {
+PArgs make_pargs(const GemmProblem& p, int mode) {
     PArgs a{};
     a.perm_src = p.perm_src;
     a.topk_w = p.topk_w;
     a.tiles = p.tiles;
-    a.n_tiles = p.n_tiles;
-    a.max_tiles = p.max_tiles;
     a.k = p.k;
     if (mode == 0) {
         a.a_src = (const uint16_t*)p.h;
@@ -363,6 +395,10 @@ PArgs make_pargs(const GemmProblem& p, int mode, int BN) {
         a.out = p.act;
         a.K = p.H;
         a.N = p.I;
+        a.work = p.work_gateup;
+        a.n_work = p.n_work_gateup;
+        a.n_ntiles = (p.I + kBNGateUp - 1) / kBNGateUp;
+        a.max_work = p.max_tiles * a.n_ntiles;
     } else {
         a.a_src = (const uint16_t*)p.act;
         a.a_bytes = (uint32_t)((size_t)p.T * p.k * p.I * 2);
@@ -373,8 +409,11 @@ PArgs make_pargs(const GemmProblem& p, int mode, int BN) {
         a.out = p.y;
         a.K = p.I;
         a.N = p.H;
+        a.work = p.work_down;
+        a.n_work = p.n_work_down;
+        a.n_ntiles = (p.H + kBNDown - 1) / kBNDown;
+        a.max_work = p.max_tiles * a.n_ntiles;
     }
-    a.n_ntiles = (a.N + BN - 1) / BN;
     return a;
 }
 
@@ -387,32 +426,47 @@ hipError_t set_smem(Kern kern, size_t bytes) {
 
 int prefill_block_m() { return kBM; }
 
+// Largest LDS footprint of the bf16-activation GEMMs for contraction depth K
+// (the MXFP4 kernels keep the tile's scales for all of K in LDS).
+size_t prefill_smem_bytes(int K, int expert_dtype) {
+    if (expert_dtype == DT_MXFP4)
+        return smem_bytes<0, DT_MXFP4, kBNGateUp>(K) > smem_bytes<1, DT_MXFP4, kBNDown>(K)
+                   ? smem_bytes<0, DT_MXFP4, kBNGateUp>(K)
+                   : smem_bytes<1, DT_MXFP4, kBNDown>(K);
+    return smem_bytes<0, DT_BF16, kBNGateUp>(K) > smem_bytes<1, DT_BF16, kBNDown>(K)
+               ? smem_bytes<0, DT_BF16, kBNGateUp>(K)
+               : smem_bytes<1, DT_BF16, kBNDown>(K);
+}
+
+int prefill_col_tiles(int N, int mode) {
+    const int bn = mode == 0 ? kBNGateUp : kBNDown;
+    return (N + bn - 1) / bn;
+}
+
+constexpr size_t kMaxSmem = 160 * 1024;
+
 hipError_t launch_gateup_bf16(const GemmProblem& p, hipStream_t stream) {
-    const PArgs a = make_pargs(p, 0, kBNGateUp);
+    const PArgs a = make_pargs(p, 0);
     if (p.expert_dtype == DT_MXFP4) {
-        constexpr size_t sm = PCfg<0, DT_MXFP4, kBNGateUp>::SMEM;
-        static const hipError_t attr = set_smem(gateup_gemm_kernel<DT_MXFP4>, sm);
+        static const hipError_t attr = set_smem(gateup_gemm_kernel<DT_MXFP4>, kMaxSmem);
         if (attr != hipSuccess) return attr;
-        return launch_k(gateup_gemm_kernel<DT_MXFP4>, sm, a, stream);
+        return launch_k(gateup_gemm_kernel<DT_MXFP4>, smem_bytes<0, DT_MXFP4, kBNGateUp>(a.K), a, stream);
     }
-    constexpr size_t sm = PCfg<0, DT_BF16, kBNGateUp>::SMEM;
-    static const hipError_t attr = set_smem(gateup_gemm_kernel<DT_BF16>, sm);
+    static const hipError_t attr = set_smem(gateup_gemm_kernel<DT_BF16>, kMaxSmem);
     if (attr != hipSuccess) return attr;
-    return launch_k(gateup_gemm_kernel<DT_BF16>, sm, a, stream);
+    return launch_k(gateup_gemm_kernel<DT_BF16>, smem_bytes<0, DT_BF16, kBNGateUp>(a.K), a, stream);
 }
 
 hipError_t launch_down_bf16(const GemmProblem& p, hipStream_t stream) {
-    const PArgs a = make_pargs(p, 1, kBNDown);
+    const PArgs a = make_pargs(p, 1);
     if (p.expert_dtype == DT_MXFP4) {
-        constexpr size_t sm = PCfg<1, DT_MXFP4, kBNDown>::SMEM;
-        static const hipError_t attr = set_smem(down_gemm_kernel<DT_MXFP4>, sm);
+        static const hipError_t attr = set_smem(down_gemm_kernel<DT_MXFP4>, kMaxSmem);
         if (attr != hipSuccess) return attr;
-        return launch_k(down_gemm_kernel<DT_MXFP4>, sm, a, stream);
+        return launch_k(down_gemm_kernel<DT_MXFP4>, smem_bytes<1, DT_MXFP4, kBNDown>(a.K), a, stream);
     }
-    constexpr size_t sm = PCfg<1, DT_BF16, kBNDown>::SMEM;
-    static const hipError_t attr = set_smem(down_gemm_kernel<DT_BF16>, sm);
+    static const hipError_t attr = set_smem(down_gemm_kernel<DT_BF16>, kMaxSmem);
     if (attr != hipSuccess) return attr;
-    return launch_k(down_gemm_kernel<DT_BF16>, sm, a, stream);
+    return launch_k(down_gemm_kernel<DT_BF16>, smem_bytes<1, DT_BF16, kBNDown>(a.K), a, stream);
 }
 
 }  // namespace moe

@@ -4,7 +4,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace {
@@ -35,8 +35,8 @@ int check_problem(const moe_problem* p) {
 
 // Workspace regions, in order.
 struct Layout {
-    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, act, y, total;
-    int nblk, max_tiles, BM;
+    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, work0, work1, act, y, total;
+    int nblk, max_tiles, BM, nc0, nc1;
 };
 
 Layout layout(const moe_problem* p) {
@@ -54,7 +54,11 @@ Layout layout(const moe_problem* p) {
     L.perm = o;     o = align_up(o + tk * 4);
     L.inv = o;      o = align_up(o + tk * 4);
     L.tiles = o;    o = align_up(o + (size_t)L.max_tiles * sizeof(Tile));
-    L.ntiles = o;   o = align_up(o + 4);
+    L.ntiles = o;   o = align_up(o + 16);  // tile count, then the two work-list counts
+    L.nc0 = moe::prefill_col_tiles(p->I, 0);
+    L.nc1 = moe::prefill_col_tiles(p->H, 1);
+    L.work0 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc0 * 4);
+    L.work1 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc1 * 4);
     L.act = o;      o = align_up(o + tk * p->I * act_bytes(p->act_dtype));
     L.y = o;        o = align_up(o + tk * p->H * 4);
     L.total = o;
@@ -157,8 +161,10 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
                            topk_w, blk, rank, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(1);
+    moe::WorkList wl0{(int32_t*)(ws + L.work0), ntiles + 1, L.nc0};
+    moe::WorkList wl1{(int32_t*)(ws + L.work1), ntiles + 2, L.nc1};
     e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
-                               L.max_tiles, stream);
+                               L.max_tiles, wl0, wl1, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(2);
 
@@ -174,6 +180,10 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     g.tiles = tiles;
     g.n_tiles = ntiles;
     g.max_tiles = L.max_tiles;
+    g.work_gateup = wl0.items;
+    g.n_work_gateup = wl0.count;
+    g.work_down = wl1.items;
+    g.n_work_down = wl1.count;
     g.act = act;
     g.y = y;
     e = moe::launch_gateup(g, stream);

@@ -147,12 +147,20 @@ hipError_t launch_router(int act_dtype, const void* h, const void* w_router, con
                          float* topk_w, int32_t* blk_counts /*[E][nblk]*/, int32_t* local_rank,
                          hipStream_t stream);
 
-// Stage 1: scan + stable permutation + tile list.
+// Stage 1: scan + stable permutation + tile list + GEMM work lists.
+// A work list enumerates (row tile, column tile) pairs as
+// tile * n_col_tiles + col_tile, grouped by expert: for each expert, for each
+// column tile, that expert's row tiles.
+struct WorkList {
+    int32_t* items;    // [max_tiles * n_col_tiles]
+    int32_t* count;    // [1]
+    int n_col_tiles;
+};
 hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx,
                              int32_t* blk_counts /*in: counts, out: bases*/,
                              const int32_t* local_rank, int32_t* offsets /*[E+1]*/,
                              int32_t* perm_src, int32_t* inv, Tile* tiles, int32_t* n_tiles,
-                             int max_tiles, hipStream_t stream);
+                             int max_tiles, WorkList w0, WorkList w1, hipStream_t stream);
 
 // Stages 2 and 3: grouped GEMMs over the tile list.
 struct GemmProblem {
@@ -170,10 +178,15 @@ struct GemmProblem {
     const Tile* tiles;
     const int32_t* n_tiles;
     int max_tiles;
+    const int32_t* work_gateup;
+    const int32_t* n_work_gateup;
+    const int32_t* work_down;
+    const int32_t* n_work_down;
     void* act;  // [T*k, I] act_dtype (expert-major rows)
     float* y;   // [T*k, H] fp32, indexed by assignment t*k+slot
 };
 int gemm_block_m(int act_dtype, int expert_dtype, int T, int k, int E);
+int prefill_col_tiles(int N, int mode);  // column tiles of the bf16 GEMMs (mode 0 gate/up, 1 down)
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, hipStream_t stream);
 

@@ -2,7 +2,7 @@
 // use while staging weight tiles (exact: every decoded value is representable
 // in bf16).  One thread per 32-element group; groups are contiguous 16-byte
 // runs of packed codes with one E8M0 scale byte each.
-#include "../../include/moe.h"
+#include "moe.h"
 #include "moe_internal.h"
 
 namespace {

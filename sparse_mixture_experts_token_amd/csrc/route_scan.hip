@@ -9,6 +9,9 @@
 //   inv[a]      the row of assignment a
 //   tiles       the (expert, first row, rows) tiles of at most BM rows that the
 //               grouped GEMMs walk; experts without tokens get no tile.
+//   work lists  the order in which the GEMM workgroups take (row tile, column
+//               tile) pairs: expert by expert, for each column tile all of the
+//               expert's row tiles.
 //
 // One workgroup of 1024 threads.  Input: the per-token-tile expert counts and
 // the within-tile ranks written by the router stage.
@@ -32,7 +35,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
                                                           const int32_t* __restrict__ local_rank,
                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                                                           int32_t* __restrict__ inv, Tile* __restrict__ tiles,
-                                                          int32_t* __restrict__ n_tiles, int max_tiles) {
+                                                          int32_t* __restrict__ n_tiles, int max_tiles, WorkList w0,
+                                                          WorkList w1) {
     __shared__ int32_t totals[1024];
     __shared__ int32_t offs[1025];
     __shared__ int32_t toff[1025];
@@ -100,6 +104,19 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
             tl.pad = 0;
             tiles[base + j] = tl;
         }
+        // work lists: this expert's (column tile, row tile) pairs, row tiles fastest
+        for (int l = 0; l < 2; ++l) {
+            const WorkList& w = l ? w1 : w0;
+            if (!w.items) continue;
+            const int nc = w.n_col_tiles;
+            int32_t* dst = w.items + (size_t)base * nc;
+            for (int c = 0; c < nc; ++c)
+                for (int j = 0; j < nt; ++j) dst[c * nt + j] = (base + j) * nc + c;
+        }
+    }
+    if (tid == 0) {
+        if (w0.count) w0.count[0] = toff[E] * w0.n_col_tiles;
+        if (w1.count) w1.count[0] = toff[E] * w1.n_col_tiles;
     }
 
     // 4. stable scatter: row = offsets[e] + (earlier tiles' count) + rank in tile
@@ -117,9 +134,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
 
 hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx, int32_t* blk_counts,
                              const int32_t* local_rank, int32_t* offsets, int32_t* perm_src, int32_t* inv,
-                             Tile* tiles, int32_t* n_tiles, int max_tiles, hipStream_t stream) {
+                             Tile* tiles, int32_t* n_tiles, int max_tiles, WorkList w0, WorkList w1,
+                             hipStream_t stream) {
     route_scan_kernel<<<1, 1024, 0, stream>>>(T, E, k, BM, topk_idx, blk_counts, local_rank, offsets, perm_src, inv,
-                                              tiles, n_tiles, max_tiles);
+                                              tiles, n_tiles, max_tiles, w0, w1);
     return hipGetLastError();
 }
 
