@@ -37,12 +37,14 @@ int check_problem(const moe_problem* p) {
 struct Layout {
     size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, work0, work1, act, y, total;
     int nblk, max_tiles, BM, nc0, nc1;
+    bool decode;
 };
 
 Layout layout(const moe_problem* p) {
     Layout L{};
     const size_t tk = (size_t)p->T * p->k;
-    L.BM = moe::gemm_block_m(p->act_dtype, p->expert_dtype, p->T, p->k, p->E);
+    L.decode = moe::decode_path(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
+    L.BM = L.decode ? moe::decode_block_m() : moe::gemm_block_m(p->act_dtype, p->expert_dtype, p->T, p->k, p->E);
     L.nblk = (p->T + moe::kRouterTokens - 1) / moe::kRouterTokens;
     L.max_tiles = (int)((tk + L.BM - 1) / L.BM) + p->E;
     size_t o = 0;
@@ -55,8 +57,8 @@ Layout layout(const moe_problem* p) {
     L.inv = o;      o = align_up(o + tk * 4);
     L.tiles = o;    o = align_up(o + (size_t)L.max_tiles * sizeof(Tile));
     L.ntiles = o;   o = align_up(o + 16);  // tile count, then the two work-list counts
-    L.nc0 = moe::prefill_col_tiles(p->I, 0);
-    L.nc1 = moe::prefill_col_tiles(p->H, 1);
+    L.nc0 = L.decode ? 0 : moe::prefill_col_tiles(p->I, 0);  // decode kernels need no work lists
+    L.nc1 = L.decode ? 0 : moe::prefill_col_tiles(p->H, 1);
     L.work0 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc0 * 4);
     L.work1 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc1 * 4);
     L.act = o;      o = align_up(o + tk * p->I * act_bytes(p->act_dtype));
@@ -161,8 +163,8 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
                            topk_w, blk, rank, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(1);
-    moe::WorkList wl0{(int32_t*)(ws + L.work0), ntiles + 1, L.nc0};
-    moe::WorkList wl1{(int32_t*)(ws + L.work1), ntiles + 2, L.nc1};
+    moe::WorkList wl0{L.decode ? nullptr : (int32_t*)(ws + L.work0), ntiles + 1, L.nc0};
+    moe::WorkList wl1{L.decode ? nullptr : (int32_t*)(ws + L.work1), ntiles + 2, L.nc1};
     e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
                                L.max_tiles, wl0, wl1, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -186,6 +188,7 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     g.n_work_down = wl1.count;
     g.act = act;
     g.y = y;
+    g.decode = L.decode;
     e = moe::launch_gateup(g, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(3);

@@ -184,8 +184,15 @@ struct GemmProblem {
     const int32_t* n_work_down;
     void* act;  // [T*k, I] act_dtype (expert-major rows)
     float* y;   // [T*k, H] fp32, indexed by assignment t*k+slot
+    bool decode;  // use the skinny (decode) kernels; tiles are decode_block_m() rows
 };
 int gemm_block_m(int act_dtype, int expert_dtype, int T, int k, int E);
+// Decode-sized problems (bf16 activations, on average at most one 16-row tile
+// per expert) take the weight-streaming kernels of gemm_decode.hip.
+bool decode_path(int act_dtype, int T, int H, int I, int E, int k);
+int decode_block_m();
+hipError_t launch_gateup_decode(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_down_decode(const GemmProblem& p, hipStream_t stream);
 int prefill_col_tiles(int N, int mode);  // column tiles of the bf16 GEMMs (mode 0 gate/up, 1 down)
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, hipStream_t stream);

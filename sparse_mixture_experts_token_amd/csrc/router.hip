@@ -23,13 +23,13 @@ namespace {
 
 constexpr int BT = kRouterTokens;  // tokens per workgroup
 constexpr int NW = 4;              // waves per workgroup
-constexpr int CB = 4;              // 16-wide expert column blocks per pass
+constexpr int kCBMax = 4;          // 16-wide expert column blocks per pass (at most)
 
 struct RouterSmem {
     // layout offsets (bytes) for a given padded expert count
     static __host__ __device__ size_t logits_off() { return 0; }
     static __host__ __device__ size_t part_off(int Ep) { return (size_t)BT * Ep * 4; }
-    static __host__ __device__ size_t selpos_off(int Ep) { return part_off(Ep) + (size_t)NW * BT * CB * 16 * 4; }
+    static __host__ __device__ size_t selpos_off(int Ep) { return part_off(Ep) + (size_t)NW * BT * kCBMax * 16 * 4; }
     static __host__ __device__ size_t bytes(int Ep) { return selpos_off(Ep) + (size_t)BT * Ep * 2; }
 };
 
@@ -42,27 +42,122 @@ __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_t* p, size_t
 
 constexpr int kNone = 0x7fffffff;
 
-// Wave-wide arg-max of (value, index): larger value wins, then lower index.
-// A lane without a candidate holds index kNone; any candidate beats it, so a
-// candidate is always found while one exists (even for NaN or -inf logits).
+// Cross-lane moves within 16-lane rows (DPP): no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
+
+__device__ __forceinline__ float lane_f(float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); }
+
+// (value, index) order: larger value wins, then lower index.  A lane without
+// a candidate holds index kNone; any candidate beats it, so a candidate is
+// always found while one exists (even for NaN or -inf logits).
+__device__ __forceinline__ void argmax_merge(float& v, int& idx, float ov, int oi) {
+    const bool take = oi != kNone && (idx == kNone || ov > v || (ov == v && oi < idx));
+    v = take ? ov : v;
+    idx = take ? oi : idx;
+}
+
+template <int CTRL>
+__device__ __forceinline__ void argmax_dpp(float& v, int& idx) {
+    argmax_merge(v, idx, dpp_f<CTRL>(v), dpp_i<CTRL>(idx));
+}
+
+// Wave-wide arg-max; the result is the same in every lane.
 __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
+    argmax_dpp<kDppXor1>(v, idx);
+    argmax_dpp<kDppXor2>(v, idx);
+    argmax_dpp<kDppHalfMirror>(v, idx);
+    argmax_dpp<kDppMirror>(v, idx);  // every lane holds its 16-lane row's result
+    float bv = lane_f(v, 0);
+    int bi = __builtin_amdgcn_readlane(idx, 0);
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        float ov = __shfl_xor(v, d, 64);
-        int oi = __shfl_xor(idx, d, 64);
-        bool take = oi != kNone && (idx == kNone || ov > v || (ov == v && oi < idx));
-        v = take ? ov : v;
-        idx = take ? oi : idx;
+    for (int r = 1; r < 4; ++r) argmax_merge(bv, bi, lane_f(v, 16 * r), __builtin_amdgcn_readlane(idx, 16 * r));
+    v = bv;
+    idx = bi;
+}
+
+// Wave-wide sum in a fixed order; the result is the same in every lane.
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);
+    x += dpp_f<kDppMirror>(x);
+    return ((lane_f(x, 0) + lane_f(x, 16)) + lane_f(x, 32)) + lane_f(x, 48);
+}
+
+// One pass over K for CB 16-wide expert column blocks starting at cb0.
+// Each wave takes the 32-wide K steps wave, wave + 4, ...; the loads of P
+// consecutive steps are issued together before their MFMAs so that a wave
+// waits for memory once per P steps.  Steps past the end load a valid address
+// and contribute zero; columns past E read row E-1 and are discarded later.
+template <typename TA, int CB>
+__device__ __forceinline__ void logits_pass(const TA* __restrict__ hrow, const TA* __restrict__ wr, int H, int E,
+                                            int cb0, int wave, int lane, f32x4 (&acc)[CB]) {
+    constexpr bool kBf16 = sizeof(TA) == 2;
+    constexpr int KSTEP = kBf16 ? 32 : 4;  // K per 16x16 MFMA
+    constexpr int P = kBf16 ? 6 : 8;       // steps per batch of loads
+    const int nsteps = H / KSTEP;
+    const TA* wrow[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+        acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int e = min((cb0 + c) * 16 + (lane & 15), E - 1);
+        wrow[c] = wr + (size_t)e * H;
+    }
+    if constexpr (kBf16) {
+        const int koff = (lane >> 4) * 8;
+        for (int s0 = wave; s0 < nsteps; s0 += NW * P) {
+            bf16x8 a[P], b[P][CB];
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                const int s = s0 + NW * q;
+                const int kk = (s < nsteps ? s : s0) * KSTEP + koff;
+                a[q] = *reinterpret_cast<const bf16x8*>(hrow + kk);
+#pragma unroll
+                for (int c = 0; c < CB; ++c) b[q][c] = *reinterpret_cast<const bf16x8*>(wrow[c] + kk);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the whole batch of loads ahead of the MFMAs
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                if (s0 + NW * q >= nsteps) a[q] = bf16x8{};
+#pragma unroll
+                for (int c = 0; c < CB; ++c) acc[c] = mfma16(a[q], b[q][c], acc[c]);
+            }
+        }
+    } else {
+        const int koff = lane >> 4;
+        for (int s0 = wave; s0 < nsteps; s0 += NW * P) {
+            float a[P], b[P][CB];
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                const int s = s0 + NW * q;
+                const int kk = (s < nsteps ? s : s0) * KSTEP + koff;
+                a[q] = hrow[kk];
+#pragma unroll
+                for (int c = 0; c < CB; ++c) b[q][c] = wrow[c][kk];
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < P; ++q) {
+                if (s0 + NW * q >= nsteps) a[q] = 0.f;
+#pragma unroll
+                for (int c = 0; c < CB; ++c) acc[c] = mfma16(a[q], b[q][c], acc[c]);
+            }
+        }
     }
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-    return x;
-}
-
-template <typename TA>
+template <typename TA, int CB, int NV>
 __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, const TA* __restrict__ wr,
                                                      const TA* __restrict__ br, int T, int H, int E, int k,
                                                      float* __restrict__ logits_opt, int32_t* __restrict__ topk_idx,
@@ -83,56 +178,20 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
     for (int i = tid; i < BT * Ep; i += 256) selpos[i] = 0;
 
     // ---------------------------------------------------------- logits --
-    constexpr bool kBf16 = sizeof(TA) == 2;
-    constexpr int KSTEP = kBf16 ? 32 : 4;  // K per 16x16 MFMA
-    const int nsteps = H / KSTEP;
     const int arow = min(t0 + (lane & 15), T - 1);
     const TA* hrow = h + (size_t)arow * H;
     const int ncb = (E + 15) >> 4;
 
     for (int cb0 = 0; cb0 < ncb; cb0 += CB) {
         f32x4 acc[CB];
-        const TA* wrow[CB];
-#pragma unroll
-        for (int c = 0; c < CB; ++c) {
-            acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-            int e = min((cb0 + c) * 16 + (lane & 15), E - 1);
-            wrow[c] = wr + (size_t)e * H;
-        }
-        if constexpr (kBf16) {
-            const int koff = (lane >> 4) * 8;
-#pragma unroll 2
-            for (int s = wave; s < nsteps; s += NW) {
-                const int kk = s * KSTEP + koff;
-                bf16x8 a = *reinterpret_cast<const bf16x8*>(hrow + kk);
-                bf16x8 b[CB];
-#pragma unroll
-                for (int c = 0; c < CB; ++c) b[c] = *reinterpret_cast<const bf16x8*>(wrow[c] + kk);
-#pragma unroll
-                for (int c = 0; c < CB; ++c)
-                    if (cb0 + c < ncb) acc[c] = mfma16(a, b[c], acc[c]);
-            }
-        } else {
-            const int koff = lane >> 4;
-#pragma unroll 4
-            for (int s = wave; s < nsteps; s += NW) {
-                const int kk = s * KSTEP + koff;
-                float a = hrow[kk];
-                float b[CB];
-#pragma unroll
-                for (int c = 0; c < CB; ++c) b[c] = wrow[c][kk];
-#pragma unroll
-                for (int c = 0; c < CB; ++c)
-                    if (cb0 + c < ncb) acc[c] = mfma16(a, b[c], acc[c]);
-            }
-        }
+        logits_pass<TA, CB>(hrow, wr, H, E, cb0, wave, lane, acc);
         // partial sums of this wave: part[wave][row][c*16 + col]
 #pragma unroll
         for (int c = 0; c < CB; ++c)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 int row = (lane >> 4) * 4 + j;
-                part[((wave * BT) + row) * (CB * 16) + c * 16 + (lane & 15)] = acc[c][j];
+                part[((wave * BT) + row) * (kCBMax * 16) + c * 16 + (lane & 15)] = acc[c][j];
             }
         __syncthreads();
         // fixed-order reduction over the waves, then the bias
@@ -141,10 +200,10 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
             int col = i % (CB * 16);
             int e = cb0 * 16 + col;
             if (e < E) {
-                float v = part[(0 * BT + row) * (CB * 16) + col];
-                v += part[(1 * BT + row) * (CB * 16) + col];
-                v += part[(2 * BT + row) * (CB * 16) + col];
-                v += part[(3 * BT + row) * (CB * 16) + col];
+                float v = part[(0 * BT + row) * (kCBMax * 16) + col];
+                v += part[(1 * BT + row) * (kCBMax * 16) + col];
+                v += part[(2 * BT + row) * (kCBMax * 16) + col];
+                v += part[(3 * BT + row) * (kCBMax * 16) + col];
                 if (br) v += load_scalar(br, e);
                 s_lds[row * Ep + e] = v;
             }
@@ -153,24 +212,23 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
     }
 
     // -------------------------------------------- top-k + selected softmax --
-    constexpr int NV = 16;  // up to 1024 experts: lane owns e = lane + 64 i
-    const int nv = Ep >> 6;
+    // Lane owns experts e = lane + 64 i, i < NV (NV = padded E / 64).
     for (int tt = wave; tt < BT; tt += NW) {
         const int t = t0 + tt;
         if (t >= T) break;  // wave-uniform
-        float v[NV], orig[NV];
+        float orig[NV];
+        uint32_t live = 0;  // bit i: expert lane + 64 i exists
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            int e = lane + 64 * i;
-            float x = (i < nv && e < E) ? s_lds[tt * Ep + e] : -INFINITY;
-            v[i] = x;
-            orig[i] = x;
+            const int e = lane + 64 * i;
+            const bool ok = e < E;
+            orig[i] = ok ? s_lds[tt * Ep + e] : -INFINITY;
+            live |= ok ? (1u << i) : 0u;
         }
         if (logits_opt) {
-            for (int i = 0; i < nv; ++i) {
-                int e = lane + 64 * i;
-                if (e < E) logits_opt[(size_t)t * E + e] = orig[i];
-            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if ((live >> i) & 1u) logits_opt[(size_t)t * E + lane + 64 * i] = orig[i];
         }
         uint32_t selmask = 0;
         float smax = 0.f;
@@ -179,11 +237,10 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
             int bi = kNone;
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
-                int e = lane + 64 * i;
-                bool live = i < nv && e < E && !((selmask >> i) & 1u);
-                bool take = live && (bi == kNone || v[i] > bv);  // ascending e: ties keep the lower index
-                bv = take ? v[i] : bv;
-                bi = take ? e : bi;
+                const bool cand = ((live & ~selmask) >> i) & 1u;
+                const bool take = cand && (bi == kNone || orig[i] > bv);  // ascending e: ties keep the lower index
+                bv = take ? orig[i] : bv;
+                bi = take ? lane + 64 * i : bi;
             }
             wave_argmax(bv, bi);
             if (r == 0) smax = bv;
@@ -201,7 +258,8 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
         // position in ascending expert order
         int before = 0;
         const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        for (int i = 0; i < nv; ++i) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
             const bool sel = (selmask >> i) & 1u;
             const uint64_t bal = __ballot(sel);
             if (sel) {
@@ -228,28 +286,48 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
     }
 }
 
+template <typename TA, int CB, int NV>
+hipError_t launch_k(const void* h, const void* w_router, const void* b_router, int T, int H, int E, int k,
+                    float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, int32_t* local_rank,
+                    hipStream_t stream) {
+    const int nblk = (T + BT - 1) / BT;
+    const size_t smem = RouterSmem::bytes((E + 63) & ~63);
+    auto kern = router_kernel<TA, CB, NV>;
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)RouterSmem::bytes(1024));
+    if (attr != hipSuccess) return attr;
+    kern<<<nblk, 256, smem, stream>>>((const TA*)h, (const TA*)w_router, (const TA*)b_router, T, H, E, k, logits_opt,
+                                      topk_idx, topk_w, blk_counts, local_rank);
+    return hipGetLastError();
+}
+
+// Instantiation by expert count: CB column blocks per logits pass, NV experts per lane in top-k.
+template <typename TA>
+hipError_t launch_t(const void* h, const void* w_router, const void* b_router, int T, int H, int E, int k,
+                    float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, int32_t* local_rank,
+                    hipStream_t stream) {
+#define MOE_ROUTER_LAUNCH(CB, NV)                                                                                  \
+    return launch_k<TA, CB, NV>(h, w_router, b_router, T, H, E, k, logits_opt, topk_idx, topk_w, blk_counts, \
+                                local_rank, stream)
+    if (E <= 16) MOE_ROUTER_LAUNCH(1, 1);
+    if (E <= 32) MOE_ROUTER_LAUNCH(2, 1);
+    if (E <= 64) MOE_ROUTER_LAUNCH(4, 1);
+    if (E <= 128) MOE_ROUTER_LAUNCH(4, 2);
+    if (E <= 256) MOE_ROUTER_LAUNCH(4, 4);
+    MOE_ROUTER_LAUNCH(4, 16);
+#undef MOE_ROUTER_LAUNCH
+}
+
 }  // namespace
 
 hipError_t launch_router(int act_dtype, const void* h, const void* w_router, const void* b_router, int T, int H,
                          int E, int k, float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* blk_counts,
                          int32_t* local_rank, hipStream_t stream) {
-    const int nblk = (T + BT - 1) / BT;
-    const int Ep = (E + 63) & ~63;
-    const size_t smem = RouterSmem::bytes(Ep);
-    if (act_dtype == DT_BF16) {
-        (void)hipFuncSetAttribute((const void*)router_kernel<uint16_t>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)smem);
-        router_kernel<uint16_t><<<nblk, 256, smem, stream>>>(
-            (const uint16_t*)h, (const uint16_t*)w_router, (const uint16_t*)b_router, T, H, E, k, logits_opt, topk_idx,
-            topk_w, blk_counts, local_rank);
-    } else {
-        (void)hipFuncSetAttribute((const void*)router_kernel<float>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)smem);
-        router_kernel<float><<<nblk, 256, smem, stream>>>((const float*)h, (const float*)w_router,
-                                                          (const float*)b_router, T, H, E, k, logits_opt, topk_idx,
-                                                          topk_w, blk_counts, local_rank);
-    }
-    return hipGetLastError();
+    if (act_dtype == DT_BF16)
+        return launch_t<uint16_t>(h, w_router, b_router, T, H, E, k, logits_opt, topk_idx, topk_w, blk_counts,
+                                  local_rank, stream);
+    return launch_t<float>(h, w_router, b_router, T, H, E, k, logits_opt, topk_idx, topk_w, blk_counts, local_rank,
+                           stream);
 }
 
 size_t router_smem_bytes(int E) { return RouterSmem::bytes((E + 63) & ~63); }

@@ -64,6 +64,11 @@ EDGE = [
     synth.Config(107, "f32-tails", T=77, H=192, I=320, E=5, k=2, act="f32", expert="f32", bias_std=0.01),
     synth.Config(108, "many-tiles-per-expert", T=1500, H=64, I=128, E=3, k=2, act="bf16", expert="bf16"),
     synth.Config(109, "1024-experts", T=40, H=64, I=64, E=1024, k=9, act="bf16", expert="bf16"),
+    # decode-sized (at most 16 rows per expert on average): the weight-streaming kernels
+    synth.Config(110, "decode-K-tails", T=24, H=192, I=320, E=8, k=2, act="bf16", expert="bf16"),
+    synth.Config(111, "decode-mxfp4-K-tails", T=20, H=192, I=320, E=6, k=3, act="bf16", expert="mxfp4"),
+    synth.Config(112, "decode-several-tiles-per-expert", T=64, H=128, I=128, E=8, k=2, act="bf16", expert="bf16"),
+    synth.Config(113, "decode-one-token", T=1, H=256, I=192, E=16, k=4, act="bf16", expert="mxfp4"),
 ]
 
 
