@@ -6,10 +6,12 @@
 //   p_i = exp(s_i - max_S) / sum_{j in S_t} exp(s_j - max_S)
 //
 // Logits use 16x16 MFMA tiles (tokens x experts) with fp32 accumulation.  The
-// K range (hidden) is split over the four waves by interleaved 32-wide steps
-// and the four partial sums are added in a fixed order, so every expert column
-// goes through exactly the same sequence of operations: two identical router
-// rows (silent copies) give bitwise-identical logits.
+// K range (hidden) is split over the sixteen waves by interleaved 32-wide
+// steps (so a wave needs about one batch of loads for H = 2880) and the
+// sixteen partial sums are added in a fixed order, so every expert column goes
+// through exactly the same sequence of operations: two identical router rows
+// (silent copies) give bitwise-identical logits.  Top-k then takes one token
+// per wave: k rounds of a wave-wide arg-max over DPP lane moves.
 //
 // Besides topk_idx / topk_w the kernel writes, for the stable expert-major
 // permutation built by the next stage:
@@ -22,15 +24,21 @@ namespace moe {
 namespace {
 
 constexpr int BT = kRouterTokens;  // tokens per workgroup
-constexpr int NW = 4;              // waves per workgroup
+constexpr int NW = 16;             // waves per workgroup
+constexpr int kThreads = NW * 64;
 constexpr int kCBMax = 4;          // 16-wide expert column blocks per pass (at most)
 
 struct RouterSmem {
     // layout offsets (bytes) for a given padded expert count
     static __host__ __device__ size_t logits_off() { return 0; }
     static __host__ __device__ size_t part_off(int Ep) { return (size_t)BT * Ep * 4; }
-    static __host__ __device__ size_t selpos_off(int Ep) { return part_off(Ep) + (size_t)NW * BT * kCBMax * 16 * 4; }
-    static __host__ __device__ size_t bytes(int Ep) { return selpos_off(Ep) + (size_t)BT * Ep * 2; }
+    static __host__ __device__ size_t part_bytes() { return (size_t)NW * BT * kCBMax * 16 * 4; }
+    // selection positions [BT][Ep] u16 reuse the partial-sum region once the logits are done
+    static __host__ __device__ size_t selpos_off(int Ep) { return part_off(Ep); }
+    static __host__ __device__ size_t bytes(int Ep) {
+        const size_t sel = (size_t)BT * Ep * 2;
+        return part_off(Ep) + (sel > part_bytes() ? sel : part_bytes());
+    }
 };
 
 template <typename TA>
@@ -105,7 +113,7 @@ __device__ __forceinline__ void logits_pass(const TA* __restrict__ hrow, const T
                                             int cb0, int wave, int lane, f32x4 (&acc)[CB]) {
     constexpr bool kBf16 = sizeof(TA) == 2;
     constexpr int KSTEP = kBf16 ? 32 : 4;  // K per 16x16 MFMA
-    constexpr int P = kBf16 ? 6 : 8;       // steps per batch of loads
+    constexpr int P = kBf16 ? (CB == 4 ? 3 : 6) : 8;  // steps per batch of loads (register budget)
     const int nsteps = H / KSTEP;
     const TA* wrow[CB];
 #pragma unroll
@@ -158,7 +166,7 @@ __device__ __forceinline__ void logits_pass(const TA* __restrict__ hrow, const T
 }
 
 template <typename TA, int CB, int NV>
-__global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, const TA* __restrict__ wr,
+__global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__ h, const TA* __restrict__ wr,
                                                      const TA* __restrict__ br, int T, int H, int E, int k,
                                                      float* __restrict__ logits_opt, int32_t* __restrict__ topk_idx,
                                                      float* __restrict__ topk_w, int32_t* __restrict__ blk_counts,
@@ -174,8 +182,6 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
     const int lane = tid & 63;
     const int t0 = blockIdx.x * BT;
     const int nblk = gridDim.x;
-
-    for (int i = tid; i < BT * Ep; i += 256) selpos[i] = 0;
 
     // ---------------------------------------------------------- logits --
     const int arow = min(t0 + (lane & 15), T - 1);
@@ -195,21 +201,22 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
             }
         __syncthreads();
         // fixed-order reduction over the waves, then the bias
-        for (int i = tid; i < BT * CB * 16; i += 256) {
+        for (int i = tid; i < BT * CB * 16; i += kThreads) {
             int row = i / (CB * 16);
             int col = i % (CB * 16);
             int e = cb0 * 16 + col;
             if (e < E) {
-                float v = part[(0 * BT + row) * (kCBMax * 16) + col];
-                v += part[(1 * BT + row) * (kCBMax * 16) + col];
-                v += part[(2 * BT + row) * (kCBMax * 16) + col];
-                v += part[(3 * BT + row) * (kCBMax * 16) + col];
+                float v = part[row * (kCBMax * 16) + col];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) v += part[(w * BT + row) * (kCBMax * 16) + col];
                 if (br) v += load_scalar(br, e);
                 s_lds[row * Ep + e] = v;
             }
         }
         __syncthreads();
     }
+    for (int i = tid; i < BT * Ep; i += kThreads) selpos[i] = 0;
+    __syncthreads();
 
     // -------------------------------------------- top-k + selected softmax --
     // Lane owns experts e = lane + 64 i, i < NV (NV = padded E / 64).
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(256) void router_kernel(const TA* __restrict__ h, c
 
     // ---------------------------------- per-tile counts and local ranks --
     const int tcount = min(BT, T - t0);
-    for (int e = tid; e < E; e += 256) {
+    for (int e = tid; e < E; e += kThreads) {
         int running = 0;
         for (int tt = 0; tt < tcount; ++tt) {
             int sp = selpos[tt * Ep + e];
@@ -296,7 +303,7 @@ hipError_t launch_k(const void* h, const void* w_router, const void* b_router, i
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)RouterSmem::bytes(1024));
     if (attr != hipSuccess) return attr;
-    kern<<<nblk, 256, smem, stream>>>((const TA*)h, (const TA*)w_router, (const TA*)b_router, T, H, E, k, logits_opt,
+    kern<<<nblk, kThreads, smem, stream>>>((const TA*)h, (const TA*)w_router, (const TA*)b_router, T, H, E, k, logits_opt,
                                       topk_idx, topk_w, blk_counts, local_rank);
     return hipGetLastError();
 }
