@@ -7,33 +7,40 @@
 //   down:     y[a, :]   = p_a * (act[r, :] W_down[e]^T),            a = perm_src[r]
 //
 // Workgroup tile: BM = 256 rows of one expert x BN weight rows per matrix,
-// eight waves in a 4 x 2 layout (two waves per SIMD).  Wave (wm, wn) owns the
-// 32-row blocks wm and wm + 4 (interleaved, so a short row tile still splits
-// evenly) and columns wn*BN/2 .. (wn+1)*BN/2 of every matrix, as 32x32x16
-// bf16 MFMA tiles with fp32 accumulators (gate/up: 2 x 3 tiles of gate and
-// the matching 2 x 3 of up = 192 accumulators, so SiLU*up is formed in
-// registers; down: 2 x 5 = 160).  BN = 192 (gate/up) and 320 (down) divide
-// 2880 exactly.  From one wave the 32x32x16 form issues at about twice the
-// rate of the 16x16x32 form on this hardware; 256-row tiles halve the weight
-// traffic of 128-row ones.
+// four waves in a 2 x 2 layout (one per SIMD).  Wave (wm, wn) owns the 32-row
+// blocks wm, wm + 2, wm + 4, wm + 6 (interleaved, so a short row tile still
+// splits evenly) and columns wn*BN/2 .. (wn+1)*BN/2 of every matrix, as
+// 32x32x16 bf16 MFMA tiles with fp32 accumulators held in the accumulation
+// registers (gate/up: 4 x 2 tiles of gate and the matching 4 x 2 of up = 256
+// accumulators, so SiLU*up is formed in registers; down: 4 x 3 = 192).
+// BN = 128 (gate/up; the last column tile of 2880 is half full) and 192
+// (down; 15 x 192 = 2880).  A wave computes 16 (12) MFMAs per 16-deep K half
+// from 8 (7) operand fragments.
 //
 // K is swept 32 at a time through a ring of 3 LDS stages filled by
-// buffer-to-LDS DMA loads (no staging registers), two stages in flight.
-// A stage holds every operand fragment as one 1 KB block in fragment order:
-// for K half s of the stage, lane l of the 32x32x16 MFMA reads bytes
-// 16l..16l+15 of its block, i.e. row (or weight column) l mod 32 and K
-// elements 16s + 8(l/32) .. +7.  Fragment reads are thus linear
-// (conflict-free), and each DMA instruction writes one block linearly while
-// its lanes fetch the matching rows from memory.
+// buffer-to-LDS DMA loads (no staging registers).  A stage holds every operand
+// fragment as one 1 KB block in fragment order: for K half s of the stage,
+// lane l of the 32x32x16 MFMA reads bytes 16l..16l+15 of its block, i.e. row
+// (or weight column) l mod 32 and K elements 16s + 8(l/32) .. +7.  Fragment
+// reads are thus linear (conflict-free), and each DMA instruction writes one
+// block linearly while its lanes fetch the matching rows from memory.
+//
+// Software pipeline, per stage kt: the fragments of half 1 are read while the
+// MFMAs of half 0 run; then (stage kt+1 landed, one barrier) the DMA of stage
+// kt+3 is issued into the slot stage kt has just released and the fragments
+// of stage kt+1's half 0 are read while the MFMAs of half 1 run.  Two stages
+// are in flight behind the one being computed, and the matrix cores never
+// wait for an LDS round trip that could have been issued earlier.
 //
 // MXFP4 weights are staged packed (fragment order in 4-byte slots, 256-byte
 // blocks) with the tile's scales for all of K, and decoded exactly to bf16 in
-// registers right before the MFMAs.
+// registers as their fragments are read.
 //
-// A wave whose 32-row blocks are empty skips their MFMAs (branch-free loop
-// instantiations for 2, 1 or 0 live blocks; all take the same barriers).
-// Every wave issues the same number of DMA loads per stage (padded with loads
-// into a scratch block), so one vmcnt threshold serves all of them.
+// A wave whose 32-row blocks are partly past the tile's end runs a loop
+// instantiation for 4, 2 or 1 blocks (rows past the end are computed from a
+// valid row and discarded); all take the same barriers.  Every wave issues
+// the same number of DMA loads per stage (padded with loads into a scratch
+// block), so one vmcnt threshold serves all of them.
 //
 // Block order: each XCD (blocks are dealt round-robin to 8) gets a contiguous
 // range of a work list built with the routing tables: experts in order, for
@@ -46,14 +53,14 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = 8;
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
 constexpr int kBM = 256;
 constexpr int kBK = 32;      // K per LDS stage
 constexpr int kStages = 3;   // LDS ring depth (two stages in flight)
 constexpr int kXcds = 8;
-constexpr int kBNGateUp = 192;
-constexpr int kBNDown = 320;
+constexpr int kBNGateUp = 128;
+constexpr int kBNDown = 192;
 
 struct PArgs {
     const uint16_t* a_src;  // h (gate/up) or act (down), bf16
@@ -84,11 +91,21 @@ __device__ __forceinline__ void dma4(buf_rsrc r, unsigned char* lds_block, uint3
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-    else static_assert(N == 0, "add the count");
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+
+// Wait until this wave's DMA loads of all but the last `ahead` stages issued
+// have landed (each stage is DPS loads per lane).
+template <int DPS>
+__device__ __forceinline__ void wait_stages_ahead(int ahead) {
+    if (ahead >= 3) wait_vmcnt<3 * DPS>();
+    else if (ahead == 2) wait_vmcnt<2 * DPS>();
+    else if (ahead == 1) wait_vmcnt<DPS>();
+    else wait_vmcnt<0>();
+}
+
+__device__ __forceinline__ void wait_lds_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Workgroup barrier without the release fence of __syncthreads(): that fence
 // would wait for every DMA load in flight (they count as LDS writes).  Callers
@@ -106,7 +123,7 @@ template <int MODE, int WDT, int BN>
 struct PCfg {
     static constexpr bool MX = WDT == DT_MXFP4;
     static constexpr int NMAT = MODE == 0 ? 2 : 1;
-    static constexpr int MBW = 2;                     // 32-row blocks per wave
+    static constexpr int MBW = 4;                     // 32-row blocks per wave
     static constexpr int BPM = BN / 32;               // 32-column blocks per matrix
     static constexpr int NBW = BPM / 2;               // 32-column blocks per wave per matrix
     static constexpr int A_BLK = (kBM / 32) * 2;      // activation blocks per stage (row blocks x 2 K halves)
@@ -130,7 +147,7 @@ struct Srcs {
     buf_rsrc s[2];  // MXFP4 scales of those matrices
 };
 
-// Weight block b = wave + 8i (over both matrices; b >= B_BLK is a padding load).
+// Weight block b = wave + 4i (over both matrices; b >= B_BLK is a padding load).
 template <class C>
 __device__ __forceinline__ void dma_stage(const Srcs& src, unsigned char* smem, int kt, int wave,
                                           const uint32_t (&a_voff)[C::A_DMA], const uint32_t (&b_voff)[C::B_DMA],
@@ -177,50 +194,62 @@ __device__ __forceinline__ bf16x8 w_frag(const unsigned char* st, const unsigned
     }
 }
 
-// The MFMAs of one 32-deep stage for this wave's MB live 32-row blocks,
-// one 16-deep half at a time (fragments of a half are read, then used).
+// Operand fragments of one 16-deep K half for this wave: MB activation blocks
+// (row blocks wm + 2i) and NMAT x NBW weight blocks.
+template <class C, int MB>
+struct Frags {
+    bf16x8 a[MB];
+    bf16x8 b[C::NMAT][C::NBW];
+};
+
 template <class C, int BN, int MB>
-__device__ __forceinline__ void mma_stage(const unsigned char* st, const unsigned char* scales, int kg, int kt,
-                                          int wm, int wn, int lane, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
-    if constexpr (MB == 0) {
-        return;
-    } else {
+__device__ __forceinline__ void read_frags(const unsigned char* st, const unsigned char* scales, int kg, int kt, int s,
+                                           int wm, int wn, int lane, Frags<C, MB>& f) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            bf16x8 af[MB];
-            bf16x8 bfr[C::NMAT][C::NBW];
+    for (int i = 0; i < MB; ++i)
+        f.a[i] = *reinterpret_cast<const bf16x8*>(st + ((wm + 2 * i) * 2 + s) * 1024 + lane * 16);
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-                af[i] = *reinterpret_cast<const bf16x8*>(st + ((wm + 4 * i) * 2 + s) * 1024 + lane * 16);
+    for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
-            for (int m = 0; m < C::NMAT; ++m)
-#pragma unroll
-                for (int j = 0; j < C::NBW; ++j) bfr[m][j] = w_frag<C>(st, scales, kg, kt, m, wn * C::NBW + j, s, lane, BN);
-#pragma unroll
-            for (int m = 0; m < C::NMAT; ++m)
-#pragma unroll
-                for (int j = 0; j < C::NBW; ++j)
-#pragma unroll
-                    for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(af[i], bfr[m][j], acc[m][i][j]);
-        }
-    }
+        for (int j = 0; j < C::NBW; ++j) f.b[m][j] = w_frag<C>(st, scales, kg, kt, m, wn * C::NBW + j, s, lane, BN);
 }
 
+template <class C, int MB>
+__device__ __forceinline__ void mma_half(const Frags<C, MB>& f, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+#pragma unroll
+    for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < C::NBW; ++j)
+#pragma unroll
+            for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(f.a[i], f.b[m][j], acc[m][i][j]);
+}
+
+// Stages 0 .. min(3, nk) - 1 were issued by the caller.
 template <class C, int BN, int MB>
 __device__ __forceinline__ void main_loop(const Srcs& src, unsigned char* smem, const unsigned char* scales, int nk,
                                           int wave, int lane, const uint32_t (&a_voff)[C::A_DMA],
                                           const uint32_t (&b_voff)[C::B_DMA], const int (&b_mat)[C::B_DMA],
                                           f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
     const int wm = wave >> 1, wn = wave & 1;
+    Frags<C, MB> f0, f1;
+    // stage 0 landed for every thread
+    wait_stages_ahead<C::DMA_PER_STAGE>(min(nk, kStages) - 1);
+    bare_barrier();
+    read_frags<C, BN, MB>(smem, scales, nk, 0, 0, wm, wn, lane, f0);
     for (int kt = 0; kt < nk; ++kt) {
-        // stage kt landed for this thread (the next one may still be in flight) ...
-        if (kt + kStages - 2 < nk) wait_vmcnt<(kStages - 2) * C::DMA_PER_STAGE>();
-        else wait_vmcnt<0>();
-        // ... and for every thread; everyone is also done reading stage kt - 1
-        // (each wave waited for its fragment reads before its MFMAs).
-        bare_barrier();
-        if (kt + kStages - 1 < nk) dma_stage<C>(src, smem, kt + kStages - 1, wave, a_voff, b_voff, b_mat);
-        mma_stage<C, BN, MB>(smem + (kt % kStages) * C::STAGE, scales, nk, kt, wm, wn, lane, acc);
+        const unsigned char* st = smem + (kt % kStages) * C::STAGE;
+        read_frags<C, BN, MB>(st, scales, nk, kt, 1, wm, wn, lane, f1);
+        mma_half<C, MB>(f0, acc);
+        if (kt + 1 < nk) {
+            // stage kt+1 landed here and (barrier) for every thread; every wave
+            // has also finished reading stage kt, whose slot the next DMA reuses
+            wait_stages_ahead<C::DMA_PER_STAGE>(min(nk - 1, kt + kStages - 1) - (kt + 1));
+            wait_lds_reads();
+            bare_barrier();
+            if (kt + kStages < nk) dma_stage<C>(src, smem, kt + kStages, wave, a_voff, b_voff, b_mat);
+            read_frags<C, BN, MB>(smem + ((kt + 1) % kStages) * C::STAGE, scales, nk, kt + 1, 0, wm, wn, lane, f0);
+        }
+        mma_half<C, MB>(f1, acc);
     }
 }
 
@@ -244,13 +273,15 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
     const int K = args.K, N = args.N;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;   // 4 x 2 waves
+    // the wave index as a scalar: everything derived from it (DMA block
+    // addresses, weight matrix choice) stays in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wm = wave >> 1, wn = wave & 1;   // 2 x 2 waves
     const int fr = lane & 31;   // row / column within a 32-block
     const int fh = lane >> 5;   // which 8 of the 16 K elements of a half
 
     // ---- DMA sources (byte offsets) ----
-    // activation block b = wave + 8i: row block b / 2, K half b % 2
+    // activation block b = wave + 4i: row block b / 2, K half b % 2
     uint32_t a_voff[C::A_DMA];
 #pragma unroll
     for (int i = 0; i < C::A_DMA; ++i) {
@@ -277,7 +308,7 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
         src.w[1] = MODE == 0 ? make_rsrc((const unsigned char*)args.w1 + (size_t)e * wbytes, wbytes) : src.w[0];
         src.s[0] = src.s[1] = src.w[0];
     }
-    // weight block b = wave + 8i over both matrices: matrix b / (2 BPM), then
+    // weight block b = wave + 4i over both matrices: matrix b / (2 BPM), then
     // column block (b mod 2 BPM) / 2 and K half b mod 2; padding loads repeat block 0
     uint32_t b_voff[C::B_DMA];
     int b_mat[C::B_DMA];
@@ -294,9 +325,9 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
     }
 
     const int nk = K / kBK;
-    // prologue: the first kStages-1 stages in flight
+    // prologue: the first kStages stages in flight
 #pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
+    for (int s = 0; s < kStages; ++s)
         if (s < nk) dma_stage<C>(src, smem, s, wave, a_voff, b_voff, b_mat);
 
     // MXFP4: this tile's scales for the whole K range, [matrix][column][K/32]
@@ -322,19 +353,19 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[m][i][j][v] = 0.f;
 
-    // This wave's live 32-row blocks: wm and wm + 4 below ceil(rows / 32).
+    // This wave's live 32-row blocks: wm + 2i below ceil(rows / 32).
     const int live32 = (rows + 31) >> 5;
-    const int mine = (wm < live32 ? 1 : 0) + (wm + 4 < live32 ? 1 : 0);
-    if (mine == 2) main_loop<C, BN, 2>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
-    else if (mine == 1) main_loop<C, BN, 1>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
-    else main_loop<C, BN, 0>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    const int mine = live32 > wm ? (live32 - wm + 1) / 2 : 0;
+    if (mine > 2) main_loop<C, BN, 4>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    else if (mine == 2) main_loop<C, BN, 2>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    else main_loop<C, BN, 1>(src, smem, scales, nk, wave, lane, a_voff, b_voff, b_mat, acc);
 
     // ---- epilogue ----
 #pragma unroll
     for (int i = 0; i < C::MBW; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int r = (wm + 4 * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
+            const int r = (wm + 2 * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
             if (r >= rows) continue;
             if constexpr (MODE == 0) {
                 uint16_t* orow = reinterpret_cast<uint16_t*>(args.out) + (size_t)(row0 + r) * N;
@@ -358,12 +389,12 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
 }
 
 template <int WDT>
-__global__ __launch_bounds__(kThreads) void gateup_gemm_kernel(PArgs args) {
+__global__ __launch_bounds__(kThreads, 1) void gateup_gemm_kernel(PArgs args) {
     gemm_body<0, WDT, kBNGateUp>(args);
 }
 
 template <int WDT>
-__global__ __launch_bounds__(kThreads) void down_gemm_kernel(PArgs args) {
+__global__ __launch_bounds__(kThreads, 1) void down_gemm_kernel(PArgs args) {
     gemm_body<1, WDT, kBNDown>(args);
 }
 

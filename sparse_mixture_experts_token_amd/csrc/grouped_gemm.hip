@@ -330,19 +330,25 @@ int prefill_block_m();
 hipError_t launch_gateup_bf16(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down_bf16(const GemmProblem& p, hipStream_t stream);
 
-int gemm_block_m(int act_dtype, int, int, int, int) { return act_dtype == DT_F32 ? kBM : prefill_block_m(); }
+int gemm_block_m(int act_dtype, int expert_dtype, int, int, int) {
+    if (act_dtype == DT_F32) return kBM;
+    return expert_dtype == DT_MXFP4 ? prefill_block_m() : bf16_block_m();
+}
 
 // fp32 activations take the generic kernel; bf16 activations the decode kernels
-// (few rows per expert) or the prefill ones.
+// (few rows per expert) or the prefill ones (gemm_bf16.hip for bf16 weights,
+// gemm_prefill.hip for MXFP4 weights).
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream) {
     if (p.act_dtype == DT_F32) return launch_on<0, float, DT_F32, kBM, kBNGateUp>(make_args(p, 0), stream);
     if (p.decode) return launch_gateup_decode(p, stream);
+    if (p.expert_dtype == DT_BF16) return launch_gateup_bf16w(p, stream);
     return launch_gateup_bf16(p, stream);
 }
 
 hipError_t launch_down(const GemmProblem& p, hipStream_t stream) {
     if (p.act_dtype == DT_F32) return launch_on<1, float, DT_F32, kBM, kBNDown>(make_args(p, 1), stream);
     if (p.decode) return launch_down_decode(p, stream);
+    if (p.expert_dtype == DT_BF16) return launch_down_bf16w(p, stream);
     return launch_down_bf16(p, stream);
 }
 

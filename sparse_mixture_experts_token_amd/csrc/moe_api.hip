@@ -57,8 +57,10 @@ Layout layout(const moe_problem* p) {
     L.inv = o;      o = align_up(o + tk * 4);
     L.tiles = o;    o = align_up(o + (size_t)L.max_tiles * sizeof(Tile));
     L.ntiles = o;   o = align_up(o + 16);  // tile count, then the two work-list counts
-    L.nc0 = L.decode ? 0 : moe::prefill_col_tiles(p->I, 0);  // decode kernels need no work lists
-    L.nc1 = L.decode ? 0 : moe::prefill_col_tiles(p->H, 1);
+    // column tiles of the prefill work lists (the decode kernels need none)
+    const bool bf16w = p->act_dtype == MOE_BF16 && p->expert_dtype == MOE_BF16;
+    L.nc0 = L.decode ? 0 : bf16w ? moe::bf16_col_tiles(p->I, 0) : moe::prefill_col_tiles(p->I, 0);
+    L.nc1 = L.decode ? 0 : bf16w ? moe::bf16_col_tiles(p->H, 1) : moe::prefill_col_tiles(p->H, 1);
     L.work0 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc0 * 4);
     L.work1 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc1 * 4);
     L.act = o;      o = align_up(o + tk * p->I * act_bytes(p->act_dtype));

@@ -187,6 +187,11 @@ struct GemmProblem {
     bool decode;  // use the skinny (decode) kernels; tiles are decode_block_m() rows
 };
 int gemm_block_m(int act_dtype, int expert_dtype, int T, int k, int E);
+// bf16-weight prefill kernels (gemm_bf16.hip)
+int bf16_block_m();
+int bf16_col_tiles(int N, int mode);
+hipError_t launch_gateup_bf16w(const GemmProblem& p, hipStream_t stream);
+hipError_t launch_down_bf16w(const GemmProblem& p, hipStream_t stream);
 // Decode-sized problems (bf16 activations, on average at most one 16-row tile
 // per expert) take the weight-streaming kernels of gemm_decode.hip.
 bool decode_path(int act_dtype, int T, int H, int I, int E, int k);
