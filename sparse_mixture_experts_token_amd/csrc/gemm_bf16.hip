@@ -43,12 +43,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kBM = 128;
+constexpr int kBM = 256;
 constexpr int kBK = 64;      // K per LDS stage: 128 bytes of each row
-constexpr int kStages = 3;
 constexpr int kXcds = 8;
 constexpr int kBNGateUp = 128;
-constexpr int kBNDown = 192;
+constexpr int kBNDown = 128;
+constexpr int kStagesGateUp = 2;  // 64 KB stages
+constexpr int kStagesDown = 3;    // 48 KB stages
 
 struct BArgs {
     const uint16_t* a_src;  // h (gate/up) or act (down)
@@ -96,10 +97,11 @@ __device__ __forceinline__ void bare_barrier() {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int MODE, int BN>
+template <int MODE, int BN, int S>
 struct Cfg {
     static constexpr int NMAT = MODE == 0 ? 2 : 1;
-    static constexpr int MBW = 2;                    // 32-row groups per wave
+    static constexpr int NST = S;                    // LDS ring depth
+    static constexpr int MBW = kBM / 64;             // 32-row groups per wave
     static constexpr int BPM = BN / 32;              // 32-row weight groups per matrix
     static constexpr int NBW = BPM / 2;              // per wave per matrix
     static constexpr int A_BLK = kBM / 8;            // 8-row DMA blocks of activations
@@ -109,16 +111,18 @@ struct Cfg {
     static constexpr int DPS = A_DMA + B_DMA;        // DMA loads per lane per stage
     static constexpr int A_BYTES = A_BLK * 1024;
     static constexpr int STAGE = A_BYTES + B_BLK * 1024;
-    static constexpr int SMEM = kStages * STAGE;
+    static constexpr int SMEM = S * STAGE;
     static_assert(A_BLK % kWaves == 0 && B_BLK % kWaves == 0, "DMA blocks must split evenly over the waves");
     static_assert(BPM % 2 == 0, "weight rows must split over two waves");
     static_assert(SMEM <= 160 * 1024, "LDS");
+    static_assert(NMAT * MBW * NBW * 16 <= 256, "accumulators");
 };
 
-template <class C>
-struct Frags {
-    bf16x8 a[C::MBW];
-    bf16x8 b[C::NMAT][C::NBW];
+// Fragments of two consecutive K steps for this wave's MB row groups.
+template <class C, int MB>
+struct Frags2 {
+    bf16x8 a[2][MB];
+    bf16x8 b[2][C::NMAT][C::NBW];
 };
 
 // Fragments of K step q: lane offset within a 4-block (32-row) group.
@@ -128,26 +132,34 @@ __device__ __forceinline__ uint32_t frag_lane_off(int lane, int q) {
     return (uint32_t)((r >> 3) * 1024 + rb * 128 + ((c ^ rb ^ ((r >> 3) & 1)) * 16));
 }
 
+// Read the fragments of steps q0, q0+1 of stage `st`.
 template <class C, int BN, int MB>
-__device__ __forceinline__ void read_frags(const unsigned char* st, uint32_t loff, int wm, int wn, Frags<C>& f) {
+__device__ __forceinline__ void read_frags2(const unsigned char* st, const uint32_t (&loff)[4], int q0, int wm, int wn,
+                                            Frags2<C, MB>& f) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(st + (wm + 2 * i) * 4096 + loff);
+    for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int m = 0; m < C::NMAT; ++m)
+        for (int i = 0; i < MB; ++i)
+            f.a[h][i] = *reinterpret_cast<const bf16x8*>(st + (wm + 2 * i) * 4096 + loff[q0 + h]);
 #pragma unroll
-        for (int j = 0; j < C::NBW; ++j)
-            f.b[m][j] = *reinterpret_cast<const bf16x8*>(st + C::A_BYTES + (m * (BN / 32) + wn * C::NBW + j) * 4096 +
-                                                         loff);
+        for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+            for (int j = 0; j < C::NBW; ++j)
+                f.b[h][m][j] = *reinterpret_cast<const bf16x8*>(st + C::A_BYTES +
+                                                                (m * (BN / 32) + wn * C::NBW + j) * 4096 + loff[q0 + h]);
+    }
 }
 
 template <class C, int MB>
-__device__ __forceinline__ void mma_step(const Frags<C>& f, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+__device__ __forceinline__ void mma2(const Frags2<C, MB>& f, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
 #pragma unroll
-    for (int m = 0; m < C::NMAT; ++m)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int j = 0; j < C::NBW; ++j)
+        for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
-            for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(f.a[i], f.b[m][j], acc[m][i][j]);
+            for (int j = 0; j < C::NBW; ++j)
+#pragma unroll
+                for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(f.a[h][i], f.b[h][m][j], acc[m][i][j]);
 }
 
 struct Srcs {
@@ -160,7 +172,7 @@ template <class C>
 __device__ __forceinline__ void dma_stage(const Srcs& src, unsigned char* smem, int kt, int wave,
                                           const uint32_t (&a_voff)[C::A_DMA], const uint32_t (&b_voff)[C::B_DMA],
                                           const int (&b_mat)[C::B_DMA]) {
-    unsigned char* st = smem + (kt % kStages) * C::STAGE;
+    unsigned char* st = smem + (kt % C::NST) * C::STAGE;
     const uint32_t k0 = (uint32_t)kt * kBK * 2;  // bytes
 #pragma unroll
     for (int i = 0; i < C::A_DMA; ++i) dma16(src.a, st + (wave + kWaves * i) * 1024, a_voff[i], k0);
@@ -169,7 +181,54 @@ __device__ __forceinline__ void dma_stage(const Srcs& src, unsigned char* smem, 
         dma16(b_mat[i] ? src.w[1] : src.w[0], st + C::A_BYTES + (wave + kWaves * i) * 1024, b_voff[i], k0);
 }
 
-// Stages 0 .. min(kStages, nk) - 1 were issued by the caller.
+// Instruction interleaving inside one scheduling region: MFMA i is preceded
+// by its share of NV VMEM loads (the DMA) and ND LDS fragment reads, so the
+// texture unit and LDS work in the shadow of the matrix cores instead of
+// stalling the wave in a burst.
+template <int I, int NV, int ND, int NM>
+__device__ __forceinline__ void interleave() {
+    if constexpr (I < NM) {
+        constexpr int v = (I + 1) * NV / NM - I * NV / NM;
+        constexpr int d = (I + 1) * ND / NM - I * ND / NM;
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);  // VMEM read
+        if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x100, d, 0);  // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // MFMA
+        interleave<I + 1, NV, ND, NM>();
+    }
+}
+
+// One stage kt: steps 2,3 are read while steps 0,1 compute; then (stage kt+1
+// landed, one barrier: every wave is done reading stage kt) the freed slot is
+// refilled with stage kt+NST (DMA) and steps 0,1 of stage kt+1 are read while
+// steps 2,3 compute.  WAIT = stages allowed in flight at the wait (-1: read
+// `ahead` at run time).
+template <class C, int BN, int MB, bool DMA, bool NEXT, int WAIT>
+__device__ __forceinline__ void stage_iter(const Srcs& src, unsigned char* smem, int nk, int kt, int wave, int wm,
+                                           int wn, const uint32_t (&loff)[4], const uint32_t (&a_voff)[C::A_DMA],
+                                           const uint32_t (&b_voff)[C::B_DMA], const int (&b_mat)[C::B_DMA],
+                                           Frags2<C, MB>& lo, Frags2<C, MB>& hi,
+                                           f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+    constexpr int NR = 2 * (MB + C::NMAT * C::NBW);  // fragment reads per two steps
+    constexpr int NM = 2 * C::NMAT * C::NBW * MB;    // MFMAs per two steps
+    const unsigned char* st = smem + (kt % C::NST) * C::STAGE;
+    read_frags2<C, BN, MB>(st, loff, 2, wm, wn, hi);
+    mma2<C, MB>(lo, acc);
+    interleave<0, 0, NR, NM>();
+    if constexpr (NEXT) {
+        if constexpr (WAIT >= 0) wait_vmcnt<WAIT * C::DPS>();
+        else wait_stages_ahead<C::DPS>(min(nk - 1, kt + C::NST - 1) - (kt + 1));
+        wait_lds_reads();
+        bare_barrier();
+        if constexpr (DMA) dma_stage<C>(src, smem, kt + C::NST, wave, a_voff, b_voff, b_mat);
+        read_frags2<C, BN, MB>(smem + ((kt + 1) % C::NST) * C::STAGE, loff, 0, wm, wn, lo);
+        mma2<C, MB>(hi, acc);
+        interleave<0, DMA ? C::DPS : 0, NR, NM>();
+    } else {
+        mma2<C, MB>(hi, acc);
+    }
+}
+
+// Stages 0 .. min(NST, nk) - 1 were issued by the caller.
 template <class C, int BN, int MB>
 __device__ __forceinline__ void main_loop(const Srcs& src, unsigned char* smem, int nk, int wave, int lane,
                                           const uint32_t (&a_voff)[C::A_DMA], const uint32_t (&b_voff)[C::B_DMA],
@@ -178,40 +237,35 @@ __device__ __forceinline__ void main_loop(const Srcs& src, unsigned char* smem, 
     uint32_t loff[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) loff[q] = frag_lane_off(lane, q);
-    Frags<C> f0, f1;
-    wait_stages_ahead<C::DPS>(min(nk, kStages) - 1);
+    Frags2<C, MB> lo, hi;
+    wait_stages_ahead<C::DPS>(min(nk, C::NST) - 1);
     bare_barrier();
-    read_frags<C, BN, MB>(smem, loff[0], wm, wn, f0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const unsigned char* st = smem + (kt % kStages) * C::STAGE;
-        read_frags<C, BN, MB>(st, loff[1], wm, wn, f1);
-        mma_step<C, MB>(f0, acc);
-        read_frags<C, BN, MB>(st, loff[2], wm, wn, f0);
-        mma_step<C, MB>(f1, acc);
-        read_frags<C, BN, MB>(st, loff[3], wm, wn, f1);
-        mma_step<C, MB>(f0, acc);
-        if (kt + 1 < nk) {
-            // stage kt+1 landed here and (barrier) for every thread, and every
-            // wave is done reading stage kt, whose slot the next DMA refills
-            wait_stages_ahead<C::DPS>(min(nk - 1, kt + kStages - 1) - (kt + 1));
-            wait_lds_reads();
-            bare_barrier();
-            if (kt + kStages < nk) dma_stage<C>(src, smem, kt + kStages, wave, a_voff, b_voff, b_mat);
-            read_frags<C, BN, MB>(smem + ((kt + 1) % kStages) * C::STAGE, loff[0], wm, wn, f0);
-        }
-        mma_step<C, MB>(f1, acc);
-    }
+    read_frags2<C, BN, MB>(smem, loff, 0, wm, wn, lo);
+    int kt = 0;
+    // steady state: the next stage exists and a stage NST ahead is refilled
+    for (; kt + C::NST < nk; ++kt)
+        stage_iter<C, BN, MB, true, true, C::NST - 2>(src, smem, nk, kt, wave, wm, wn, loff, a_voff, b_voff, b_mat,
+                                                       lo, hi, acc);
+    for (; kt + 1 < nk; ++kt)
+        stage_iter<C, BN, MB, false, true, -1>(src, smem, nk, kt, wave, wm, wn, loff, a_voff, b_voff, b_mat, lo, hi,
+                                               acc);
+    stage_iter<C, BN, MB, false, false, 0>(src, smem, nk, kt, wave, wm, wn, loff, a_voff, b_voff, b_mat, lo, hi, acc);
 }
 
-template <int MODE, int BN>
+template <int MODE, int BN, int S>
 __device__ __forceinline__ void gemm_body(const BArgs& args) {
-    using C = Cfg<MODE, BN>;
+    using C = Cfg<MODE, BN, S>;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    // ---- block -> work item (row tile, column tile), XCD-contiguous ----
-    const int per_xcd = (args.max_work + kXcds - 1) / kXcds;
-    const int q = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (q >= args.max_work || q >= args.n_work[0]) return;
+    // ---- block -> work item (row tile, column tile) ----
+    // Blocks are dealt round-robin to the 8 XCDs; XCD x takes the x-th of 8
+    // equal contiguous ranges of the work list (sized by the actual item
+    // count, not the grid's upper bound, so every XCD gets its share).
+    const int n_work = args.n_work[0];
+    const int per_xcd = (n_work + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int q = (blockIdx.x % kXcds) * per_xcd + slot;
+    if (slot >= per_xcd || q >= n_work) return;
     const int item = args.work[q];
     const int mt = item / args.n_ntiles;
     const int nt = item % args.n_ntiles;
@@ -257,7 +311,7 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
 
     const int nk = K / kBK;
 #pragma unroll
-    for (int s = 0; s < kStages; ++s)
+    for (int s = 0; s < C::NST; ++s)
         if (s < nk) dma_stage<C>(src, smem, s, wave, a_voff, b_voff, b_mat);
 
     f32x16 acc[C::NMAT][C::MBW][C::NBW];
@@ -270,9 +324,11 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[m][i][j][v] = 0.f;
 
-    // live 32-row groups of this wave: wm and wm + 2 below ceil(rows / 32)
+    // live 32-row groups of this wave: wm + 2i below ceil(rows / 32)
     const int live32 = (rows + 31) >> 5;
-    if (live32 > wm + 2) main_loop<C, BN, 2>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    const int mine = live32 > wm ? (live32 - wm + 1) / 2 : 0;
+    if (mine > C::MBW / 2) main_loop<C, BN, C::MBW>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    else if (C::MBW > 2 && mine > 1) main_loop<C, BN, (C::MBW > 2 ? C::MBW / 2 : 1)>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
     else main_loop<C, BN, 1>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
 
     // ---- epilogue: D[v] of a 32x32 tile is row 8(v/4) + 4(l/32) + v%4, column l%32 ----
@@ -304,8 +360,12 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void gateup_bf16_kernel(BArgs args) { gemm_body<0, kBNGateUp>(args); }
-__global__ __launch_bounds__(kThreads, 1) void down_bf16_kernel(BArgs args) { gemm_body<1, kBNDown>(args); }
+using CfgGateUp = Cfg<0, kBNGateUp, kStagesGateUp>;
+using CfgDown = Cfg<1, kBNDown, kStagesDown>;
+__global__ __launch_bounds__(kThreads, 1) void gateup_bf16_kernel(BArgs args) {
+    gemm_body<0, kBNGateUp, kStagesGateUp>(args);
+}
+__global__ __launch_bounds__(kThreads, 1) void down_bf16_kernel(BArgs args) { gemm_body<1, kBNDown, kStagesDown>(args); }
 
 BArgs make_args(const GemmProblem& p, int mode) {
     BArgs a{};
@@ -354,7 +414,7 @@ int bf16_block_m() { return kBM; }
 int bf16_col_tiles(int N, int mode) { return (N + (mode == 0 ? kBNGateUp : kBNDown) - 1) / (mode == 0 ? kBNGateUp : kBNDown); }
 
 hipError_t launch_gateup_bf16w(const GemmProblem& p, hipStream_t stream) {
-    constexpr size_t smem = Cfg<0, kBNGateUp>::SMEM;
+    constexpr size_t smem = CfgGateUp::SMEM;
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)gateup_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (attr != hipSuccess) return attr;
@@ -362,7 +422,7 @@ hipError_t launch_gateup_bf16w(const GemmProblem& p, hipStream_t stream) {
 }
 
 hipError_t launch_down_bf16w(const GemmProblem& p, hipStream_t stream) {
-    constexpr size_t smem = Cfg<1, kBNDown>::SMEM;
+    constexpr size_t smem = CfgDown::SMEM;
     static const hipError_t attr =
         hipFuncSetAttribute((const void*)down_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (attr != hipSuccess) return attr;

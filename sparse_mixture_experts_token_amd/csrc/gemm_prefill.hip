@@ -259,9 +259,14 @@ __device__ __forceinline__ void gemm_body(const PArgs& args) {
     extern __shared__ __align__(16) unsigned char smem[];
 
     // ---- block -> work item (row tile, column tile) ----
-    const int per_xcd = (args.max_work + kXcds - 1) / kXcds;
-    const int q = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-    if (q >= args.max_work || q >= args.n_work[0]) return;
+    // Blocks are dealt round-robin to the 8 XCDs; XCD x takes the x-th of 8
+    // equal contiguous ranges of the work list (sized by the actual item
+    // count, not the grid's upper bound, so every XCD gets its share).
+    const int n_work = args.n_work[0];
+    const int per_xcd = (n_work + kXcds - 1) / kXcds;
+    const int slot = blockIdx.x / kXcds;
+    const int q = (blockIdx.x % kXcds) * per_xcd + slot;
+    if (slot >= per_xcd || q >= n_work) return;
     const int item = args.work[q];
     const int mt = item / args.n_ntiles;
     const int nt = item % args.n_ntiles;
