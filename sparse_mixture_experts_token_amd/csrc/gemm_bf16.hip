@@ -6,12 +6,13 @@
 //   gate/up:  act[r, :] = silu(x_r W_gate[e]^T) * (x_r W_up[e]^T),  x_r = h[token of row r]
 //   down:     y[a, :]   = p_a * (act[r, :] W_down[e]^T),            a = perm_src[r]
 //
-// Workgroup tile: BM = 128 rows of one expert x BN weight rows per matrix
-// (gate/up: 128 of gate and the same 128 of up; down: 192), four waves in a
-// 2 x 2 layout, one per SIMD.  Wave (wm, wn) owns the 32-row groups wm and
-// wm + 2 and half of the tile's weight rows of every matrix, as 32x32x16 bf16
+// Workgroup tile: BM = 256 rows of one expert x BN = 128 weight rows per
+// matrix (gate/up: 128 of gate and the same 128 of up; down: 128 of W_down),
+// eight waves in a 4 x 2 layout, two per SIMD, so that one wave's MFMAs cover
+// the other's LDS and DMA issue.  Wave (wm, wn) owns the 32-row groups wm and
+// wm + 4 and half of the tile's weight rows of every matrix, as 32x32x16 bf16
 // MFMA tiles with fp32 accumulators (gate/up: 2 x 2 of gate and 2 x 2 of up,
-// so SiLU*up is formed in registers; down: 2 x 3).
+// so SiLU*up is formed in registers; down: 2 x 2).
 //
 // Operands reach LDS by buffer-to-LDS DMA.  What limits such a kernel on this
 // hardware is how many cache lines one load instruction touches: 64 lanes x
@@ -25,11 +26,12 @@
 // 16q + 8(l/32) .. +7 of step q) spreads every group of 16 lanes over all
 // LDS banks.
 //
-// Software pipeline: three stages in the LDS ring (two in flight behind the
-// one being computed); within a stage the fragments of K step q+1 are read
-// while the MFMAs of step q run, and the one barrier per stage sits before
-// the last step, where the next stage's first fragments are read and the
-// slot just released is refilled.
+// Software pipeline: an LDS ring of two 64 KB stages (gate/up) or three 48 KB
+// stages (down).  Within a stage the fragments of K steps 2,3 are read while
+// steps 0,1 compute; then, behind the one barrier per stage, the slot just
+// released is refilled by DMA and steps 0,1 of the next stage are read while
+// steps 2,3 compute.  sched_group_barrier spreads the DMA and LDS reads
+// between the MFMAs.
 //
 // Block order: each XCD (blocks are dealt round-robin to 8) takes a
 // contiguous range of a work list built with the routing tables: experts in
@@ -41,9 +43,10 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kBM = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kWM = kWaves / 2;   // waves along the rows (2 along the weight rows)
+constexpr int kBM = 256;          // rows per tile: 8 groups of 32, 2 per wave
 constexpr int kBK = 64;      // K per LDS stage: 128 bytes of each row
 constexpr int kXcds = 8;
 constexpr int kBNGateUp = 128;
@@ -101,7 +104,7 @@ template <int MODE, int BN, int S>
 struct Cfg {
     static constexpr int NMAT = MODE == 0 ? 2 : 1;
     static constexpr int NST = S;                    // LDS ring depth
-    static constexpr int MBW = kBM / 64;             // 32-row groups per wave
+    static constexpr int MBW = kBM / (32 * kWM);     // 32-row groups per wave
     static constexpr int BPM = BN / 32;              // 32-row weight groups per matrix
     static constexpr int NBW = BPM / 2;              // per wave per matrix
     static constexpr int A_BLK = kBM / 8;            // 8-row DMA blocks of activations
@@ -140,7 +143,7 @@ __device__ __forceinline__ void read_frags2(const unsigned char* st, const uint3
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
-            f.a[h][i] = *reinterpret_cast<const bf16x8*>(st + (wm + 2 * i) * 4096 + loff[q0 + h]);
+            f.a[h][i] = *reinterpret_cast<const bf16x8*>(st + (wm + kWM * i) * 4096 + loff[q0 + h]);
 #pragma unroll
         for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
@@ -252,6 +255,20 @@ __device__ __forceinline__ void main_loop(const Srcs& src, unsigned char* smem, 
     stage_iter<C, BN, MB, false, false, 0>(src, smem, nk, kt, wave, wm, wn, loff, a_voff, b_voff, b_mat, lo, hi, acc);
 }
 
+// Main loop for the MB live row groups of this wave (MB = 1 .. MBW; a wave
+// with none computes one group from a valid row and discards it).
+template <class C, int BN, int MB>
+__device__ __forceinline__ void dispatch_mb(int mine, const Srcs& src, unsigned char* smem, int nk, int wave, int lane,
+                                            const uint32_t (&a_voff)[C::A_DMA], const uint32_t (&b_voff)[C::B_DMA],
+                                            const int (&b_mat)[C::B_DMA], f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+    if constexpr (MB == 1) {
+        main_loop<C, BN, 1>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    } else {
+        if (mine >= MB) main_loop<C, BN, MB>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+        else dispatch_mb<C, BN, MB - 1>(mine, src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    }
+}
+
 template <int MODE, int BN, int S>
 __device__ __forceinline__ void gemm_body(const BArgs& args) {
     using C = Cfg<MODE, BN, S>;
@@ -324,12 +341,10 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[m][i][j][v] = 0.f;
 
-    // live 32-row groups of this wave: wm + 2i below ceil(rows / 32)
+    // live 32-row groups of this wave: wm + kWM i below ceil(rows / 32)
     const int live32 = (rows + 31) >> 5;
-    const int mine = live32 > wm ? (live32 - wm + 1) / 2 : 0;
-    if (mine > C::MBW / 2) main_loop<C, BN, C::MBW>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
-    else if (C::MBW > 2 && mine > 1) main_loop<C, BN, (C::MBW > 2 ? C::MBW / 2 : 1)>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
-    else main_loop<C, BN, 1>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    const int mine = live32 > wm ? (live32 - wm + kWM - 1) / kWM : 0;
+    dispatch_mb<C, BN, C::MBW>(mine, src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
 
     // ---- epilogue: D[v] of a 32x32 tile is row 8(v/4) + 4(l/32) + v%4, column l%32 ----
     const int fr = lane & 31, fh = lane >> 5;
@@ -337,7 +352,7 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
     for (int i = 0; i < C::MBW; ++i) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int r = (wm + 2 * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
+            const int r = (wm + kWM * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
             if (r >= rows) continue;
             if constexpr (MODE == 0) {
                 uint16_t* orow = reinterpret_cast<uint16_t*>(args.out) + (size_t)(row0 + r) * N;
@@ -362,10 +377,10 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
 
 using CfgGateUp = Cfg<0, kBNGateUp, kStagesGateUp>;
 using CfgDown = Cfg<1, kBNDown, kStagesDown>;
-__global__ __launch_bounds__(kThreads, 1) void gateup_bf16_kernel(BArgs args) {
+__global__ __launch_bounds__(kThreads) void gateup_bf16_kernel(BArgs args) {
     gemm_body<0, kBNGateUp, kStagesGateUp>(args);
 }
-__global__ __launch_bounds__(kThreads, 1) void down_bf16_kernel(BArgs args) { gemm_body<1, kBNDown, kStagesDown>(args); }
+__global__ __launch_bounds__(kThreads) void down_bf16_kernel(BArgs args) { gemm_body<1, kBNDown, kStagesDown>(args); }
 
 BArgs make_args(const GemmProblem& p, int mode) {
     BArgs a{};
