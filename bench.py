@@ -41,10 +41,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -68,7 +68,7 @@ def measured_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        src = os.path.join(ROOT, "sparse_mixture_experts_token_amd", "csrc", "gemm_prefill.hip")
+        src = os.path.join(ROOT, "sparse_mixture_experts_token_amd", "csrc", "gemm_bf16.hip")
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
         if rec.get("source_sha256") != digest:
             return None
@@ -163,7 +163,7 @@ def main():
     g_tflops = gateup_flops(T, H, I, k) / (g_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
-                "kernel": "gateup_swiglu_gemm", "flops_per_launch": gateup_flops(T, H, I, k),
+                "kernel": "gateup_bf16_kernel (gate/up grouped GEMM + SiLU*up)", "flops_per_launch": gateup_flops(T, H, I, k),
                 "avg_launch_ms": round(g_ms, 5)}
 
     # ---- decode: first 64 tokens, HBM roofline on the touched experts' weights ----
