@@ -50,9 +50,9 @@ constexpr int kBM = 256;          // rows per tile: 8 groups of 32, 2 per wave
 constexpr int kBK = 64;      // K per LDS stage: 128 bytes of each row
 constexpr int kXcds = 8;
 constexpr int kBNGateUp = 128;
-constexpr int kBNDown = 128;
+constexpr int kBNDown = 256;
 constexpr int kStagesGateUp = 2;  // 64 KB stages
-constexpr int kStagesDown = 3;    // 48 KB stages
+constexpr int kStagesDown = 2;    // 64 KB stages
 
 struct BArgs {
     const uint16_t* a_src;  // h (gate/up) or act (down)
@@ -63,6 +63,7 @@ struct BArgs {
     const Tile* tiles;
     const int32_t* work;    // row tile * n_ntiles + column tile, expert-grouped order
     const int32_t* n_work;
+    int32_t* queue;         // [8] per-XCD work counters, zero at launch
     void* out;
     uint32_t a_bytes;
     int max_work, n_ntiles;
@@ -269,20 +270,11 @@ __device__ __forceinline__ void dispatch_mb(int mine, const Srcs& src, unsigned 
     }
 }
 
+// One work item q: (row tile, column tile) of the work list.
 template <int MODE, int BN, int S>
-__device__ __forceinline__ void gemm_body(const BArgs& args) {
+__device__ __forceinline__ void process_item(const BArgs& args, int q) {
     using C = Cfg<MODE, BN, S>;
     extern __shared__ __align__(16) unsigned char smem[];
-
-    // ---- block -> work item (row tile, column tile) ----
-    // Blocks are dealt round-robin to the 8 XCDs; XCD x takes the x-th of 8
-    // equal contiguous ranges of the work list (sized by the actual item
-    // count, not the grid's upper bound, so every XCD gets its share).
-    const int n_work = args.n_work[0];
-    const int per_xcd = (n_work + kXcds - 1) / kXcds;
-    const int slot = blockIdx.x / kXcds;
-    const int q = (blockIdx.x % kXcds) * per_xcd + slot;
-    if (slot >= per_xcd || q >= n_work) return;
     const int item = args.work[q];
     const int mt = item / args.n_ntiles;
     const int nt = item % args.n_ntiles;
@@ -375,6 +367,31 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
     }
 }
 
+// Persistent workgroups, one per CU.  Blocks are dealt round-robin to the 8
+// XCDs; XCD x owns the x-th of 8 equal contiguous ranges of the work list
+// (sized by the actual item count) and its workgroups take the range's items
+// in order from the XCD's counter, so a workgroup that drew cheap items (the
+// short last row tile of an expert) takes more of them, and the row tiles
+// sharing a weight tile still run together on one XCD.
+template <int MODE, int BN, int S>
+__device__ __forceinline__ void gemm_body(const BArgs& args) {
+    __shared__ int s_q;
+    const int n_work = args.n_work[0];
+    const int per_xcd = (n_work + kXcds - 1) / kXcds;
+    const int xcd = blockIdx.x % kXcds;
+    const int base = xcd * per_xcd;
+    const int end = min(base + per_xcd, n_work);
+    for (;;) {
+        if (threadIdx.x == 0) s_q = base + atomicAdd(args.queue + xcd, 1);
+        // s_q visible to every wave, and every wave done with the previous item's LDS
+        wait_lds_reads();
+        bare_barrier();
+        const int q = __builtin_amdgcn_readfirstlane(s_q);
+        if (q >= end) break;
+        process_item<MODE, BN, S>(args, q);
+    }
+}
+
 using CfgGateUp = Cfg<0, kBNGateUp, kStagesGateUp>;
 using CfgDown = Cfg<1, kBNDown, kStagesDown>;
 __global__ __launch_bounds__(kThreads) void gateup_bf16_kernel(BArgs args) {
@@ -398,6 +415,7 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.N = p.I;
         a.work = p.work_gateup;
         a.n_work = p.n_work_gateup;
+        a.queue = p.queues;
         a.n_ntiles = (p.I + kBNGateUp - 1) / kBNGateUp;
     } else {
         a.a_src = (const uint16_t*)p.act;
@@ -409,17 +427,30 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.N = p.H;
         a.work = p.work_down;
         a.n_work = p.n_work_down;
+        a.queue = p.queues + kXcds;
         a.n_ntiles = (p.H + kBNDown - 1) / kBNDown;
     }
     a.max_work = p.max_tiles * a.n_ntiles;
     return a;
 }
 
+// One workgroup per CU (the LDS ring allows no more), never more than the
+// work, and at least one per XCD range so that every range is drained.
+int persistent_grid(int max_work) {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    }();
+    const int g = max_work < cus ? max_work : cus;
+    return g > kXcds ? g : kXcds;
+}
+
 template <typename Kern>
 hipError_t launch(Kern kern, size_t smem, const BArgs& a, hipStream_t stream) {
-    static_assert(sizeof(Kern) > 0, "");
-    const int per_xcd = (a.max_work + kXcds - 1) / kXcds;
-    kern<<<per_xcd * kXcds, kThreads, smem, stream>>>(a);
+    kern<<<persistent_grid(a.max_work), kThreads, smem, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ int check_problem(const moe_problem* p) {
 
 // Workspace regions, in order.
 struct Layout {
-    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, work0, work1, act, y, total;
+    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, queues, work0, work1, act, y, total;
     int nblk, max_tiles, BM, nc0, nc1;
     bool decode;
 };
@@ -57,6 +57,7 @@ Layout layout(const moe_problem* p) {
     L.inv = o;      o = align_up(o + tk * 4);
     L.tiles = o;    o = align_up(o + (size_t)L.max_tiles * sizeof(Tile));
     L.ntiles = o;   o = align_up(o + 16);  // tile count, then the two work-list counts
+    L.queues = o;   o = align_up(o + moe::kNumQueues * 4);
     // column tiles of the prefill work lists (the decode kernels need none)
     const bool bf16w = p->act_dtype == MOE_BF16 && p->expert_dtype == MOE_BF16;
     L.nc0 = L.decode ? 0 : bf16w ? moe::bf16_col_tiles(p->I, 0) : moe::prefill_col_tiles(p->I, 0);
@@ -167,8 +168,9 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     mark(1);
     moe::WorkList wl0{L.decode ? nullptr : (int32_t*)(ws + L.work0), ntiles + 1, L.nc0};
     moe::WorkList wl1{L.decode ? nullptr : (int32_t*)(ws + L.work1), ntiles + 2, L.nc1};
+    int32_t* queues = (int32_t*)(ws + L.queues);
     e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
-                               L.max_tiles, wl0, wl1, stream);
+                               L.max_tiles, wl0, wl1, queues, moe::kNumQueues, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(2);
 
@@ -191,6 +193,7 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     g.act = act;
     g.y = y;
     g.decode = L.decode;
+    g.queues = queues;
     e = moe::launch_gateup(g, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(3);

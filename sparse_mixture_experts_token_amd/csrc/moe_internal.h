@@ -156,11 +156,13 @@ struct WorkList {
     int32_t* count;    // [1]
     int n_col_tiles;
 };
+// zero[0 .. n_zero-1] is cleared (the GEMMs' work-queue counters).
 hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx,
                              int32_t* blk_counts /*in: counts, out: bases*/,
                              const int32_t* local_rank, int32_t* offsets /*[E+1]*/,
                              int32_t* perm_src, int32_t* inv, Tile* tiles, int32_t* n_tiles,
-                             int max_tiles, WorkList w0, WorkList w1, hipStream_t stream);
+                             int max_tiles, WorkList w0, WorkList w1, int32_t* zero, int n_zero,
+                             hipStream_t stream);
 
 // Stages 2 and 3: grouped GEMMs over the tile list.
 struct GemmProblem {
@@ -185,7 +187,9 @@ struct GemmProblem {
     void* act;  // [T*k, I] act_dtype (expert-major rows)
     float* y;   // [T*k, H] fp32, indexed by assignment t*k+slot
     bool decode;  // use the skinny (decode) kernels; tiles are decode_block_m() rows
+    int32_t* queues;  // [16] work-queue counters (gate/up 0..7, down 8..15), zeroed by the route scan
 };
+constexpr int kNumQueues = 16;
 int gemm_block_m(int act_dtype, int expert_dtype, int T, int k, int E);
 // bf16-weight prefill kernels (gemm_bf16.hip)
 int bf16_block_m();

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                                                           int32_t* __restrict__ inv, Tile* __restrict__ tiles,
                                                           int32_t* __restrict__ n_tiles, int max_tiles, WorkList w0,
-                                                          WorkList w1) {
+                                                          WorkList w1, int32_t* __restrict__ zero, int n_zero) {
     __shared__ int32_t totals[1024];
     __shared__ int32_t offs[1025];
     __shared__ int32_t toff[1025];
@@ -47,6 +47,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int nblk = (T + kRouterTokens - 1) / kRouterTokens;
+    if (tid < n_zero) zero[tid] = 0;
 
     // 1. per expert: exclusive scan of its tile counts (in place) and its total
     for (int e = wave; e < E; e += 16) {
@@ -134,10 +135,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
 
 hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx, int32_t* blk_counts,
                              const int32_t* local_rank, int32_t* offsets, int32_t* perm_src, int32_t* inv,
-                             Tile* tiles, int32_t* n_tiles, int max_tiles, WorkList w0, WorkList w1,
-                             hipStream_t stream) {
+                             Tile* tiles, int32_t* n_tiles, int max_tiles, WorkList w0, WorkList w1, int32_t* zero,
+                             int n_zero, hipStream_t stream) {
     route_scan_kernel<<<1, 1024, 0, stream>>>(T, E, k, BM, topk_idx, blk_counts, local_rank, offsets, perm_src, inv,
-                                              tiles, n_tiles, max_tiles, w0, w1);
+                                              tiles, n_tiles, max_tiles, w0, w1, zero, n_zero);
     return hipGetLastError();
 }
 
