@@ -70,7 +70,8 @@ __device__ __forceinline__ float lane_f(float x, int l) { return __int_as_float(
 // a candidate holds index kNone; any candidate beats it, so a candidate is
 // always found while one exists (even for NaN or -inf logits).
 __device__ __forceinline__ void argmax_merge(float& v, int& idx, float ov, int oi) {
-    const bool take = oi != kNone && (idx == kNone || ov > v || (ov == v && oi < idx));
+    // non-short-circuit operators: straight-line selects, no divergent branches
+    const bool take = (oi != kNone) & ((idx == kNone) | (ov > v) | ((ov == v) & (oi < idx)));
     v = take ? ov : v;
     idx = take ? oi : idx;
 }
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
                 const bool cand = ((live & ~selmask) >> i) & 1u;
-                const bool take = cand && (bi == kNone || orig[i] > bv);  // ascending e: ties keep the lower index
+                const bool take = cand & ((bi == kNone) | (orig[i] > bv));  // ascending e: ties keep the lower index
                 bv = take ? orig[i] : bv;
                 bi = take ? lane + 64 * i : bi;
             }
