@@ -10,11 +10,12 @@ softmax, routing permutation, gate/up GEMM with SiLU*up, down GEMM with the
 routing weight, combine), from h to out.
 
 Prints one JSON line: tokens/s over the timed steps, the whole layer's
-TFLOP/s and fraction of the bf16 MFMA peak, per-stage times from HIP events
-recorded on the launch stream during the timed steps, the roofline of the
-dominant kernel (the gate/up grouped GEMM), a decode measurement (T = 64, the
-first 64 rows) against the HBM roofline, and the fp64 CPU reference timed on a
-bounded sample of the same workload.
+TFLOP/s and fraction of the bf16 MFMA peak, the roofline of the dominant
+kernel (the gate/up grouped GEMM, its launch duration from HIP events recorded
+around it on the launch stream during the timed steps), per-stage times from a
+second pass that records every stage boundary, a decode measurement (T = 64,
+the first 64 rows) against the HBM roofline, and the fp64 CPU reference timed
+on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -146,20 +147,28 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    smoe.moe_profile_begin(args.steps)
+    # timed steps: HIP events only around the dominant kernel (each event costs
+    # a few microseconds of device time) ...
+    smoe.moe_profile_begin_mask(args.steps, (1 << DOMINANT_STAGE) | (1 << (DOMINANT_STAGE + 1)))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    stage_ms, calls = smoe.moe_profile_end()
+    dom_ms, calls = smoe.moe_profile_end()
     ms_step = dt * 1e3 / args.steps
-    stage_avg = [x / calls for x in stage_ms]
+    # ... and the per-stage split from a second pass with every boundary recorded
+    smoe.moe_profile_begin(args.steps)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    stage_ms, scalls = smoe.moe_profile_end()
+    stage_avg = [x / scalls for x in stage_ms]
     F = layer_flops(T, H, I, E, k)
     tok_s = T / (dt / args.steps)
 
-    g_ms = stage_avg[DOMINANT_STAGE]
+    g_ms = dom_ms[DOMINANT_STAGE] / calls
     g_tflops = gateup_flops(T, H, I, k) / (g_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(),
@@ -212,7 +221,7 @@ def main():
                    "intermediate": I, "experts": E, "top_k": k},
         "layer_tflops": round(F / (ms_step * 1e-3) / 1e12, 2),
         "layer_mfma_frac": round(F / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "stage_ms": {smoe.moe_stage_name(i): round(x, 5) for i, x in enumerate(stage_avg)},
+        "stage_ms_profiled_pass": {smoe.moe_stage_name(i): round(x, 5) for i, x in enumerate(stage_avg)},
         "roofline": roofline, "decode": decode, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -180,6 +180,15 @@ const char *moe_status_string(int status);
  * MOE_ERR_SHAPE (n < 1), MOE_ERR_HIP. */
 #define MOE_NUM_STAGES 5
 int moe_profile_begin(int32_t max_calls);
+/* Same, recording only the stage boundaries in boundary_mask: bit i is the
+ * event before stage i, bit MOE_NUM_STAGES the one after the last stage
+ * (MOE_PROFILE_ALL = every boundary).  Each event costs a few microseconds
+ * of device time, so a timed loop can record just the stages it reports.  A
+ * stage whose two boundaries are not both recorded reads 0 in
+ * moe_profile_end.  Errors as moe_profile_begin; MOE_ERR_SHAPE also for an
+ * empty mask or bits beyond MOE_NUM_STAGES. */
+#define MOE_PROFILE_ALL ((1u << (MOE_NUM_STAGES + 1)) - 1u)
+int moe_profile_begin_mask(int32_t max_calls, uint32_t boundary_mask);
 int moe_profile_end(float stage_ms[MOE_NUM_STAGES], int32_t *calls_recorded);
 const char *moe_stage_name(int stage);
 

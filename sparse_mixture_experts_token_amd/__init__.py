@@ -12,7 +12,7 @@ The functions mirror the C entry points of ``include/moe.h``:
 * ``moe_forward(problem, weights, h, out, routing=None, workspace=None)``
 * ``moe_expand_silent(base, src, M, dst)``
 * ``moe_status_string(status)``
-* ``moe_profile_begin(max_calls)`` / ``moe_profile_end()``
+* ``moe_profile_begin(max_calls)`` / ``moe_profile_begin_mask(max_calls, mask)`` / ``moe_profile_end()``
 
 ``problem`` is a ``Problem``; ``weights`` / ``src`` / ``dst`` are dicts of
 device tensors keyed ``w_router, b_router, w_gate, w_up, w_down`` (and
@@ -35,7 +35,8 @@ MOE_NUM_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_HIP", -7: "MOE_ERR_STATE"}
 EXPORTED = ("moe_workspace_bytes", "moe_forward", "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
-            "moe_profile_begin", "moe_profile_end", "moe_stage_name")
+            "moe_profile_begin", "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name")
+MOE_PROFILE_ALL = (1 << (MOE_NUM_STAGES + 1)) - 1
 
 
 class MoeError(RuntimeError):
@@ -102,6 +103,8 @@ def load() -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_profile_begin.argtypes = [ctypes.c_int32]
     lib.moe_profile_begin.restype = ctypes.c_int
+    lib.moe_profile_begin_mask.argtypes = [ctypes.c_int32, ctypes.c_uint32]
+    lib.moe_profile_begin_mask.restype = ctypes.c_int
     lib.moe_profile_end.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)]
     lib.moe_profile_end.restype = ctypes.c_int
     lib.moe_stage_name.argtypes = [ctypes.c_int]
@@ -195,6 +198,12 @@ def moe_mxfp4_decode(packed, scales, out_bf16, stream=None) -> None:
 
 def moe_profile_begin(max_calls: int) -> None:
     _check(load().moe_profile_begin(int(max_calls)))
+
+
+def moe_profile_begin_mask(max_calls: int, boundary_mask: int) -> None:
+    """Record only the stage boundaries in ``boundary_mask`` (bit i: the event
+    before stage i; bit MOE_NUM_STAGES: the one after the last)."""
+    _check(load().moe_profile_begin_mask(int(max_calls), int(boundary_mask)))
 
 
 def moe_profile_end():

@@ -76,6 +76,7 @@ struct Profiler {
     bool armed = false;
     int max_calls = 0;
     int used = 0;
+    uint32_t mask = 0;           // stage boundaries recorded (bit i: the event before stage i)
     std::vector<hipEvent_t> ev;  // max_calls x (MOE_NUM_STAGES + 1)
 };
 Profiler& prof() {
@@ -83,11 +84,13 @@ Profiler& prof() {
     return p;
 }
 
-// Returns the event row for this call, or nullptr when not recording.
-hipEvent_t* prof_slot() {
+// Returns the event row for this call (and the boundaries to record), or
+// nullptr when not recording.
+hipEvent_t* prof_slot(uint32_t* mask) {
     Profiler& P = prof();
     std::lock_guard<std::mutex> g(P.mu);
     if (!P.armed || P.used >= P.max_calls) return nullptr;
+    *mask = P.mask;
     return &P.ev[(size_t)(P.used++) * (MOE_NUM_STAGES + 1)];
 }
 
@@ -155,9 +158,10 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     void* act = ws + L.act;
     float* y = (float*)(ws + L.y);
 
-    hipEvent_t* ev = prof_slot();
+    uint32_t ev_mask = 0;
+    hipEvent_t* ev = prof_slot(&ev_mask);
     auto mark = [&](int i) {
-        if (ev) (void)hipEventRecord(ev[i], stream);
+        if (ev && ((ev_mask >> i) & 1u)) (void)hipEventRecord(ev[i], stream);
     };
 
     hipError_t e = hipSuccess;
@@ -254,8 +258,10 @@ int moe_expand_silent(const moe_problem* base, const moe_weights* src, int32_t M
     return MOE_OK;
 }
 
-int moe_profile_begin(int32_t max_calls) {
-    if (max_calls < 1) return MOE_ERR_SHAPE;
+int moe_profile_begin(int32_t max_calls) { return moe_profile_begin_mask(max_calls, MOE_PROFILE_ALL); }
+
+int moe_profile_begin_mask(int32_t max_calls, uint32_t boundary_mask) {
+    if (max_calls < 1 || (boundary_mask & ~(uint32_t)MOE_PROFILE_ALL) != 0 || boundary_mask == 0) return MOE_ERR_SHAPE;
     Profiler& P = prof();
     std::lock_guard<std::mutex> g(P.mu);
     if (P.armed) return MOE_ERR_STATE;
@@ -269,6 +275,7 @@ int moe_profile_begin(int32_t max_calls) {
         }
     P.max_calls = max_calls;
     P.used = 0;
+    P.mask = boundary_mask;
     P.armed = true;
     return MOE_OK;
 }
@@ -279,10 +286,13 @@ int moe_profile_end(float stage_ms[MOE_NUM_STAGES], int32_t* calls_recorded) {
     if (!P.armed) return MOE_ERR_STATE;
     int rc = MOE_OK;
     float sums[MOE_NUM_STAGES] = {0};
+    int last = MOE_NUM_STAGES;  // the last boundary recorded
+    while (last > 0 && !((P.mask >> last) & 1u)) --last;
     for (int c = 0; c < P.used; ++c) {
         hipEvent_t* row = &P.ev[(size_t)c * (MOE_NUM_STAGES + 1)];
-        if (hipEventSynchronize(row[MOE_NUM_STAGES]) != hipSuccess) rc = MOE_ERR_HIP;
+        if (hipEventSynchronize(row[last]) != hipSuccess) rc = MOE_ERR_HIP;
         for (int s = 0; s < MOE_NUM_STAGES; ++s) {
+            if (!((P.mask >> s) & 1u) || !((P.mask >> (s + 1)) & 1u)) continue;
             float ms = 0.f;
             if (hipEventElapsedTime(&ms, row[s], row[s + 1]) != hipSuccess) rc = MOE_ERR_HIP;
             sums[s] += ms;
@@ -296,6 +306,7 @@ int moe_profile_end(float stage_ms[MOE_NUM_STAGES], int32_t* calls_recorded) {
     P.armed = false;
     P.used = 0;
     P.max_calls = 0;
+    P.mask = 0;
     return rc;
 }
 

@@ -20,6 +20,9 @@
 namespace moe {
 namespace {
 
+constexpr int kBaseLds = 16384;  // ints of scanned bases kept in LDS (64 KB)
+constexpr int kPer = 4;           // elements per lane per round of loads
+
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -38,6 +41,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
                                                           int32_t* __restrict__ n_tiles, int max_tiles, WorkList w0,
                                                           WorkList w1, int32_t* __restrict__ zero, int n_zero) {
     __shared__ int32_t totals[1024];
+    // the scanned per-block bases, kept here when they fit (E * nblk <= kBaseLds)
+    __shared__ int32_t base_lds[kBaseLds];
     __shared__ int32_t offs[1025];
     __shared__ int32_t toff[1025];
     __shared__ int32_t wsum[16];
@@ -49,15 +54,34 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     const int nblk = (T + kRouterTokens - 1) / kRouterTokens;
     if (tid < n_zero) zero[tid] = 0;
 
-    // 1. per expert: exclusive scan of its tile counts (in place) and its total
+    // 1. per expert: exclusive scan of its tile counts (in place) and its total.
+    //    A lane owns kPer consecutive blocks, so a row of up to 64 * kPer
+    //    counts is read in one round of loads; longer rows take more rounds.
+    const bool in_lds = E * nblk <= kBaseLds;
     for (int e = wave; e < E; e += 16) {
         int running = 0;
         int32_t* row = blk + (size_t)e * nblk;
-        for (int b0 = 0; b0 < nblk; b0 += 64) {
-            const int i = b0 + lane;
-            const int c = i < nblk ? row[i] : 0;
-            const int x = wave_incl_scan(c, lane);
-            if (i < nblk) row[i] = running + x - c;
+        for (int b0 = 0; b0 < nblk; b0 += 64 * kPer) {
+            int c[kPer];
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = b0 + lane * kPer + j;
+                c[j] = i < nblk ? row[i] : 0;
+            }
+            int sum = 0;
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) sum += c[j];
+            const int x = wave_incl_scan(sum, lane);
+            int pre = running + x - sum;  // exclusive prefix of this lane's first block
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                const int i = b0 + lane * kPer + j;
+                if (i < nblk) {
+                    row[i] = pre;
+                    if (in_lds) base_lds[e * nblk + i] = pre;
+                }
+                pre += c[j];
+            }
             running += __shfl(x, 63, 64);
         }
         if (lane == 0) totals[e] = running;
@@ -120,14 +144,28 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
         if (w1.count) w1.count[0] = toff[E] * w1.n_col_tiles;
     }
 
-    // 4. stable scatter: row = offsets[e] + (earlier tiles' count) + rank in tile
+    // 4. stable scatter: row = offsets[e] + (earlier tiles' count) + rank in tile.
+    //    Loads of kPer assignments are issued together.
     const int total = T * k;
-    for (int a = tid; a < total; a += 1024) {
-        const int e = topk_idx[a];
-        const int b = (a / k) / kRouterTokens;
-        const int r = offs[e] + blk[(size_t)e * nblk + b] + local_rank[a];
-        perm_src[r] = a;
-        inv[a] = r;
+    for (int a0 = 0; a0 < total; a0 += 1024 * kPer) {
+        int e[kPer], lr[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int a = a0 + j * 1024 + tid;
+            e[j] = a < total ? topk_idx[a] : 0;
+            lr[j] = a < total ? local_rank[a] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int a = a0 + j * 1024 + tid;
+            if (a < total) {
+                const int b = (a / k) / kRouterTokens;
+                const size_t bi = (size_t)e[j] * nblk + b;
+                const int r = offs[e[j]] + (in_lds ? base_lds[bi] : blk[bi]) + lr[j];
+                perm_src[r] = a;
+                inv[a] = r;
+            }
+        }
     }
 }
 

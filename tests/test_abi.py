@@ -20,7 +20,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = smoe.load()
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(smoe.EXPORTED) == names
@@ -97,3 +97,10 @@ def test_profile_end_without_begin_is_a_state_error():
     lib = smoe.load()
     assert lib.moe_profile_end(None, None) == -7
     assert lib.moe_profile_begin(0) == -2
+
+
+def test_profile_mask_argument_errors():
+    lib = smoe.load()
+    assert lib.moe_profile_begin_mask(4, 0) == -2                                  # empty mask
+    assert lib.moe_profile_begin_mask(4, smoe.MOE_PROFILE_ALL + 1) == -2          # bit beyond the last boundary
+    assert lib.moe_profile_begin_mask(0, smoe.MOE_PROFILE_ALL) == -2              # no calls

@@ -254,3 +254,16 @@ def test_profile_hooks_report_every_stage():
     assert calls == 3 and len(ms) == 5 and all(x > 0 for x in ms)
     with pytest.raises(smoe.MoeError):
         smoe.moe_profile_end()
+
+
+def test_profile_mask_records_only_selected_stages():
+    L, st = layer_full(1)
+    prob = problem(L.cfg, 64)
+    w = device_weights(L, st)
+    h = to_dev(L.h, "f32")
+    out = torch.empty((64, 64), device="cuda")
+    smoe.moe_profile_begin_mask(2, (1 << 2) | (1 << 3))   # the gate/up stage only
+    for _ in range(2):
+        smoe.moe_forward(prob, w, h, out)
+    ms, calls = smoe.moe_profile_end()
+    assert calls == 2 and ms[2] > 0 and all(ms[i] == 0 for i in (0, 1, 3, 4))
