@@ -71,7 +71,8 @@ enum {
  *   I  intermediate_size              E  num_local_experts
  *   k  num_experts_per_tok
  * Supported: T >= 0 (T = 0 is a no-op), 1 <= k <= E <= 1024, H and I positive
- * multiples of 64, T*k*max(H,I) < 2^31, H*I < 2^29.
+ * multiples of 64, T*k*max(H,I) < 2^31, H*I < 2^29; with MXFP4 experts also
+ * H, I <= 4992 (a GEMM tile keeps its scales for the whole contraction on chip).
  * Supported dtype pairs (act_dtype, expert_dtype): (F32, F32), (BF16, BF16),
  * (BF16, MXFP4).  act_dtype is the format of h, out, w_router and b_router. */
 typedef struct {

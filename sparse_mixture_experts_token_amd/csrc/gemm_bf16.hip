@@ -1,5 +1,5 @@
-// Stages 2 and 3 for bf16 activations and bf16 expert weights: the experts'
-// SwiGLU networks as grouped GEMMs over expert-major row tiles
+// Stages 2 and 3 for bf16 activations and bf16 or MXFP4 expert weights: the
+// experts' SwiGLU networks as grouped GEMMs over expert-major row tiles
 // ("gpt-oss 20B" field guide, cutaway 03: SwiGLU experts, weighted sum;
 // "openai/gpt-oss-20b" fixture comparison: hidden_act silu).
 //
@@ -33,6 +33,16 @@
 // steps 2,3 compute.  sched_group_barrier spreads the DMA and LDS reads
 // between the MFMAs.
 //
+// MXFP4 weights ("gpt-oss-20b and gpt-oss-120b" explainer, "Four-bit expert
+// weights"; element and scale encodings of OCP MX v1.0) travel packed: a
+// stage holds each weight row's 32 bytes of codes for its 64 K in 32-row 1 KB
+// blocks (lane l of a DMA fetches row l/2, half l%2).  That pattern is four
+// times slower per byte than whole-line fetches but carries a quarter of the
+// bytes, and the smaller stages leave room for a three-stage ring beside the
+// tile's E8M0 scales for all of K.  A fragment is 4 bytes of codes plus its
+// scale, decoded exactly to bf16 right before its MFMA (hardware scaled
+// conversion for scales 2..252, integer path for the extremes).
+//
 // Block order: each XCD (blocks are dealt round-robin to 8) takes a
 // contiguous range of a work list built with the routing tables: experts in
 // order, for each expert its column tiles, for each column tile all the
@@ -56,8 +66,10 @@ constexpr int kStagesDown = 2;    // 64 KB stages
 
 struct BArgs {
     const uint16_t* a_src;  // h (gate/up) or act (down)
-    const void* w0;         // gate or down, [E][N][K]
+    const void* w0;         // gate or down, [E][N][K] bf16 or [E][N][K/2] MXFP4 codes
     const void* w1;         // up
+    const uint8_t* s0;      // MXFP4 scales [E][N][K/32] of w0, w1
+    const uint8_t* s1;
     const int32_t* perm_src;
     const float* topk_w;
     const Tile* tiles;
@@ -101,32 +113,50 @@ __device__ __forceinline__ void bare_barrier() {
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-template <int MODE, int BN, int S>
+template <int MODE, int BN, int S, bool MXW>
 struct Cfg {
+    static constexpr bool MX = MXW;                  // MXFP4 weights
     static constexpr int NMAT = MODE == 0 ? 2 : 1;
     static constexpr int NST = S;                    // LDS ring depth
     static constexpr int MBW = kBM / (32 * kWM);     // 32-row groups per wave
     static constexpr int BPM = BN / 32;              // 32-row weight groups per matrix
     static constexpr int NBW = BPM / 2;              // per wave per matrix
     static constexpr int A_BLK = kBM / 8;            // 8-row DMA blocks of activations
-    static constexpr int B_BLK = NMAT * BN / 8;      // of weights
+    // weights: bf16 in 8-row blocks (128 bytes a row), MXFP4 codes in
+    // 32-row blocks (the 32 bytes of codes a row holds for 64 K)
+    static constexpr int B_BLK = MX ? NMAT * BN / 32 : NMAT * BN / 8;
     static constexpr int A_DMA = A_BLK / kWaves;     // per wave per stage
     static constexpr int B_DMA = B_BLK / kWaves;
     static constexpr int DPS = A_DMA + B_DMA;        // DMA loads per lane per stage
     static constexpr int A_BYTES = A_BLK * 1024;
     static constexpr int STAGE = A_BYTES + B_BLK * 1024;
-    static constexpr int SMEM = S * STAGE;
+    static constexpr int SMEM = S * STAGE;  // + the tile's MXFP4 scales for all of K
+    static constexpr size_t smem(int K) { return (size_t)SMEM + (MX ? (size_t)NMAT * BN * (K / 32) : 0); }
     static_assert(A_BLK % kWaves == 0 && B_BLK % kWaves == 0, "DMA blocks must split evenly over the waves");
     static_assert(BPM % 2 == 0, "weight rows must split over two waves");
     static_assert(SMEM <= 160 * 1024, "LDS");
     static_assert(NMAT * MBW * NBW * 16 <= 256, "accumulators");
 };
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Weight operand of one fragment: bf16 values, or for MXFP4 the raw 8 codes
+// and their scale (decoded right before the MFMA, which halves the registers
+// the read-ahead needs).
+template <bool MX>
+struct WFrag {
+    bf16x8 v;
+};
+template <>
+struct WFrag<true> {
+    u32x2 v;  // codes, scale
+};
+
 // Fragments of two consecutive K steps for this wave's MB row groups.
 template <class C, int MB>
 struct Frags2 {
     bf16x8 a[2][MB];
-    bf16x8 b[2][C::NMAT][C::NBW];
+    WFrag<C::MX> b[2][C::NMAT][C::NBW];
 };
 
 // Fragments of K step q: lane offset within a 4-block (32-row) group.
@@ -136,10 +166,37 @@ __device__ __forceinline__ uint32_t frag_lane_off(int lane, int q) {
     return (uint32_t)((r >> 3) * 1024 + rb * 128 + ((c ^ rb ^ ((r >> 3) & 1)) * 16));
 }
 
-// Read the fragments of steps q0, q0+1 of stage `st`.
+// MXFP4: 8 codes (4 bytes) and their E8M0 scale -> 8 bf16, exactly.
+__device__ __forceinline__ bf16x8 mx_frag(uint32_t q, uint32_t scale) {
+    u32x4 v;
+    if (scale >= 2u && scale <= 252u) {
+        const float sc = __uint_as_float(scale << 23);
+        v = u32x4{cvt_fp4x2_bf16x2(q, sc, 0), cvt_fp4x2_bf16x2(q, sc, 1), cvt_fp4x2_bf16x2(q, sc, 2),
+                  cvt_fp4x2_bf16x2(q, sc, 3)};
+    } else {
+        uint32_t w[4];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const uint32_t byte = (q >> (8 * bb)) & 0xffu;
+            w[bb] = e2m1_to_bf16_exact(byte & 0xfu, scale) | (e2m1_to_bf16_exact(byte >> 4, scale) << 16);
+        }
+        v = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Where a lane's MXFP4 operand lives: block row l%32, and within the row's
+// 32 bytes of codes for this stage the 4 bytes of K elements 16q + 8(l/32).
+struct MxLane {
+    uint32_t code_off;   // r * 32 + 4 * (l / 32)  (+ 8q per step)
+    uint32_t scale_row;  // r * kg
+};
+
+// Read the fragments of steps q0, q0+1 of stage kt (held at `st`).
 template <class C, int BN, int MB>
 __device__ __forceinline__ void read_frags2(const unsigned char* st, const uint32_t (&loff)[4], int q0, int wm, int wn,
-                                            Frags2<C, MB>& f) {
+                                            Frags2<C, MB>& f, const unsigned char* scales, int kg, int kt,
+                                            MxLane mxl) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -148,9 +205,18 @@ __device__ __forceinline__ void read_frags2(const unsigned char* st, const uint3
 #pragma unroll
         for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
-            for (int j = 0; j < C::NBW; ++j)
-                f.b[h][m][j] = *reinterpret_cast<const bf16x8*>(st + C::A_BYTES +
-                                                                (m * (BN / 32) + wn * C::NBW + j) * 4096 + loff[q0 + h]);
+            for (int j = 0; j < C::NBW; ++j) {
+                const int grp = m * (BN / 32) + wn * C::NBW + j;  // 32-row weight group
+                if constexpr (C::MX) {
+                    const int q = q0 + h;
+                    const uint32_t codes = *reinterpret_cast<const uint32_t*>(st + C::A_BYTES + grp * 1024 +
+                                                                              mxl.code_off + 8 * q);
+                    const uint32_t scale = scales[(uint32_t)grp * 32u * (uint32_t)kg + mxl.scale_row + 2 * kt + q / 2];
+                    f.b[h][m][j].v = u32x2{codes, scale};
+                } else {
+                    f.b[h][m][j].v = *reinterpret_cast<const bf16x8*>(st + C::A_BYTES + grp * 4096 + loff[q0 + h]);
+                }
+            }
     }
 }
 
@@ -161,14 +227,19 @@ __device__ __forceinline__ void mma2(const Frags2<C, MB>& f, f32x16 (&acc)[C::NM
 #pragma unroll
         for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
-            for (int j = 0; j < C::NBW; ++j)
+            for (int j = 0; j < C::NBW; ++j) {
+                bf16x8 b;
+                if constexpr (C::MX) b = mx_frag(f.b[h][m][j].v.x, f.b[h][m][j].v.y);
+                else b = f.b[h][m][j].v;
 #pragma unroll
-                for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(f.a[h][i], f.b[h][m][j], acc[m][i][j]);
+                for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(f.a[h][i], b, acc[m][i][j]);
+            }
 }
 
 struct Srcs {
     buf_rsrc a;
     buf_rsrc w[2];
+    buf_rsrc s[2];  // MXFP4 scales
 };
 
 // Block b of a stage is filled by wave b % 4; a wave's blocks are b = wave + 4i.
@@ -180,9 +251,10 @@ __device__ __forceinline__ void dma_stage(const Srcs& src, unsigned char* smem, 
     const uint32_t k0 = (uint32_t)kt * kBK * 2;  // bytes
 #pragma unroll
     for (int i = 0; i < C::A_DMA; ++i) dma16(src.a, st + (wave + kWaves * i) * 1024, a_voff[i], k0);
+    const uint32_t kb = C::MX ? (uint32_t)kt * (kBK / 2) : k0;  // bytes of codes or bf16 per row
 #pragma unroll
     for (int i = 0; i < C::B_DMA; ++i)
-        dma16(b_mat[i] ? src.w[1] : src.w[0], st + C::A_BYTES + (wave + kWaves * i) * 1024, b_voff[i], k0);
+        dma16(b_mat[i] ? src.w[1] : src.w[0], st + C::A_BYTES + (wave + kWaves * i) * 1024, b_voff[i], kb);
 }
 
 // Instruction interleaving inside one scheduling region: MFMA i is preceded
@@ -201,21 +273,31 @@ __device__ __forceinline__ void interleave() {
     }
 }
 
+// Everything a work item's main loop needs besides the accumulators.
+template <class C>
+struct ItemCtx {
+    Srcs src;
+    uint32_t a_voff[C::A_DMA];  // this lane's DMA source offsets in stage 0
+    uint32_t b_voff[C::B_DMA];
+    int b_mat[C::B_DMA];
+    const unsigned char* scales;  // MXFP4: the tile's scales in LDS, [NMAT*BN][kg]
+    int kg;                       // K / 32
+    MxLane mxl;
+};
+
 // One stage kt: steps 2,3 are read while steps 0,1 compute; then (stage kt+1
 // landed, one barrier: every wave is done reading stage kt) the freed slot is
 // refilled with stage kt+NST (DMA) and steps 0,1 of stage kt+1 are read while
 // steps 2,3 compute.  WAIT = stages allowed in flight at the wait (-1: read
 // `ahead` at run time).
 template <class C, int BN, int MB, bool DMA, bool NEXT, int WAIT>
-__device__ __forceinline__ void stage_iter(const Srcs& src, unsigned char* smem, int nk, int kt, int wave, int wm,
-                                           int wn, const uint32_t (&loff)[4], const uint32_t (&a_voff)[C::A_DMA],
-                                           const uint32_t (&b_voff)[C::B_DMA], const int (&b_mat)[C::B_DMA],
-                                           Frags2<C, MB>& lo, Frags2<C, MB>& hi,
+__device__ __forceinline__ void stage_iter(const ItemCtx<C>& x, unsigned char* smem, int nk, int kt, int wave, int wm,
+                                           int wn, const uint32_t (&loff)[4], Frags2<C, MB>& lo, Frags2<C, MB>& hi,
                                            f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
     constexpr int NR = 2 * (MB + C::NMAT * C::NBW);  // fragment reads per two steps
     constexpr int NM = 2 * C::NMAT * C::NBW * MB;    // MFMAs per two steps
     const unsigned char* st = smem + (kt % C::NST) * C::STAGE;
-    read_frags2<C, BN, MB>(st, loff, 2, wm, wn, hi);
+    read_frags2<C, BN, MB>(st, loff, 2, wm, wn, hi, x.scales, x.kg, kt, x.mxl);
     mma2<C, MB>(lo, acc);
     interleave<0, 0, NR, NM>();
     if constexpr (NEXT) {
@@ -223,8 +305,9 @@ __device__ __forceinline__ void stage_iter(const Srcs& src, unsigned char* smem,
         else wait_stages_ahead<C::DPS>(min(nk - 1, kt + C::NST - 1) - (kt + 1));
         wait_lds_reads();
         bare_barrier();
-        if constexpr (DMA) dma_stage<C>(src, smem, kt + C::NST, wave, a_voff, b_voff, b_mat);
-        read_frags2<C, BN, MB>(smem + ((kt + 1) % C::NST) * C::STAGE, loff, 0, wm, wn, lo);
+        if constexpr (DMA) dma_stage<C>(x.src, smem, kt + C::NST, wave, x.a_voff, x.b_voff, x.b_mat);
+        read_frags2<C, BN, MB>(smem + ((kt + 1) % C::NST) * C::STAGE, loff, 0, wm, wn, lo, x.scales, x.kg, kt + 1,
+                               x.mxl);
         mma2<C, MB>(hi, acc);
         interleave<0, DMA ? C::DPS : 0, NR, NM>();
     } else {
@@ -234,46 +317,42 @@ __device__ __forceinline__ void stage_iter(const Srcs& src, unsigned char* smem,
 
 // Stages 0 .. min(NST, nk) - 1 were issued by the caller.
 template <class C, int BN, int MB>
-__device__ __forceinline__ void main_loop(const Srcs& src, unsigned char* smem, int nk, int wave, int lane,
-                                          const uint32_t (&a_voff)[C::A_DMA], const uint32_t (&b_voff)[C::B_DMA],
-                                          const int (&b_mat)[C::B_DMA], f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+__device__ __forceinline__ void main_loop(const ItemCtx<C>& x, unsigned char* smem, int nk, int wave, int lane,
+                                          f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
     const int wm = wave >> 1, wn = wave & 1;
     uint32_t loff[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) loff[q] = frag_lane_off(lane, q);
     Frags2<C, MB> lo, hi;
     wait_stages_ahead<C::DPS>(min(nk, C::NST) - 1);
+    wait_lds_reads();  // MXFP4: this wave's scale writes
     bare_barrier();
-    read_frags2<C, BN, MB>(smem, loff, 0, wm, wn, lo);
+    read_frags2<C, BN, MB>(smem, loff, 0, wm, wn, lo, x.scales, x.kg, 0, x.mxl);
     int kt = 0;
     // steady state: the next stage exists and a stage NST ahead is refilled
     for (; kt + C::NST < nk; ++kt)
-        stage_iter<C, BN, MB, true, true, C::NST - 2>(src, smem, nk, kt, wave, wm, wn, loff, a_voff, b_voff, b_mat,
-                                                       lo, hi, acc);
-    for (; kt + 1 < nk; ++kt)
-        stage_iter<C, BN, MB, false, true, -1>(src, smem, nk, kt, wave, wm, wn, loff, a_voff, b_voff, b_mat, lo, hi,
-                                               acc);
-    stage_iter<C, BN, MB, false, false, 0>(src, smem, nk, kt, wave, wm, wn, loff, a_voff, b_voff, b_mat, lo, hi, acc);
+        stage_iter<C, BN, MB, true, true, C::NST - 2>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
+    for (; kt + 1 < nk; ++kt) stage_iter<C, BN, MB, false, true, -1>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
+    stage_iter<C, BN, MB, false, false, 0>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
 }
 
 // Main loop for the MB live row groups of this wave (MB = 1 .. MBW; a wave
 // with none computes one group from a valid row and discards it).
 template <class C, int BN, int MB>
-__device__ __forceinline__ void dispatch_mb(int mine, const Srcs& src, unsigned char* smem, int nk, int wave, int lane,
-                                            const uint32_t (&a_voff)[C::A_DMA], const uint32_t (&b_voff)[C::B_DMA],
-                                            const int (&b_mat)[C::B_DMA], f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+__device__ __forceinline__ void dispatch_mb(int mine, const ItemCtx<C>& x, unsigned char* smem, int nk, int wave,
+                                            int lane, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
     if constexpr (MB == 1) {
-        main_loop<C, BN, 1>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+        main_loop<C, BN, 1>(x, smem, nk, wave, lane, acc);
     } else {
-        if (mine >= MB) main_loop<C, BN, MB>(src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
-        else dispatch_mb<C, BN, MB - 1>(mine, src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+        if (mine >= MB) main_loop<C, BN, MB>(x, smem, nk, wave, lane, acc);
+        else dispatch_mb<C, BN, MB - 1>(mine, x, smem, nk, wave, lane, acc);
     }
 }
 
 // One work item q: (row tile, column tile) of the work list.
-template <int MODE, int BN, int S>
+template <int MODE, int BN, int S, bool MXW>
 __device__ __forceinline__ void process_item(const BArgs& args, int q) {
-    using C = Cfg<MODE, BN, S>;
+    using C = Cfg<MODE, BN, S, MXW>;
     extern __shared__ __align__(16) unsigned char smem[];
     const int item = args.work[q];
     const int mt = item / args.n_ntiles;
@@ -288,11 +367,15 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wm = wave >> 1, wn = wave & 1;
-    const int rb = lane >> 3;                                  // row within a DMA block
+    const int rb = lane >> 3;                                  // row within an 8-row DMA block
     const uint32_t chunk_even = (uint32_t)((lane & 7) ^ rb);  // logical 16-byte chunk fetched (even block)
 
+    ItemCtx<C> x;
+    x.kg = K / 32;
+    x.scales = smem + C::SMEM;
+    x.mxl.code_off = (uint32_t)((lane & 31) * 32 + 4 * (lane >> 5));
+    x.mxl.scale_row = (uint32_t)((lane & 31) * x.kg);
     // ---- DMA sources: byte offsets of this lane's chunk in stage 0 ----
-    uint32_t a_voff[C::A_DMA];
 #pragma unroll
     for (int i = 0; i < C::A_DMA; ++i) {
         const int blk = wave + kWaves * i;
@@ -301,27 +384,47 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
         int src_row;
         if constexpr (MODE == 0) src_row = args.perm_src[row0 + rr] / args.k;
         else src_row = row0 + rr;
-        a_voff[i] = (uint32_t)src_row * (uint32_t)K * 2u + (chunk_even ^ (uint32_t)(blk & 1)) * 16u;
+        x.a_voff[i] = (uint32_t)src_row * (uint32_t)K * 2u + (chunk_even ^ (uint32_t)(blk & 1)) * 16u;
     }
-    Srcs src;
-    src.a = make_rsrc(args.a_src, args.a_bytes);
-    const uint32_t wbytes = (uint32_t)((size_t)N * K * 2);
-    src.w[0] = make_rsrc((const unsigned char*)args.w0 + (size_t)e * wbytes, wbytes);
-    src.w[1] = MODE == 0 ? make_rsrc((const unsigned char*)args.w1 + (size_t)e * wbytes, wbytes) : src.w[0];
-    uint32_t b_voff[C::B_DMA];
-    int b_mat[C::B_DMA];
+    x.src.a = make_rsrc(args.a_src, args.a_bytes);
+    if constexpr (C::MX) {
+        const uint32_t wb = (uint32_t)((size_t)N * K / 2), sb = (uint32_t)((size_t)N * K / 32);
+        x.src.w[0] = make_rsrc((const unsigned char*)args.w0 + (size_t)e * wb, wb);
+        x.src.w[1] = MODE == 0 ? make_rsrc((const unsigned char*)args.w1 + (size_t)e * wb, wb) : x.src.w[0];
+        x.src.s[0] = make_rsrc(args.s0 + (size_t)e * sb, sb);
+        x.src.s[1] = MODE == 0 ? make_rsrc(args.s1 + (size_t)e * sb, sb) : x.src.s[0];
+        // 32-row blocks of codes: lane l fetches row l/2, bytes 16(l%2)..+15 of the stage's 32
 #pragma unroll
-    for (int i = 0; i < C::B_DMA; ++i) {
-        const int blk = wave + kWaves * i;
-        b_mat[i] = (blk * 8) / BN;
-        const int n = min(n0 + (blk * 8) % BN + rb, N - 1);
-        b_voff[i] = (uint32_t)n * (uint32_t)K * 2u + (chunk_even ^ (uint32_t)(blk & 1)) * 16u;
+        for (int i = 0; i < C::B_DMA; ++i) {
+            const int blk = wave + kWaves * i;
+            x.b_mat[i] = (blk * 32) / BN;
+            const int n = min(n0 + (blk * 32) % BN + (lane >> 1), N - 1);
+            x.b_voff[i] = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(lane & 1) * 16u;
+        }
+        // the tile's scales for all of K: [matrix][BN rows][kg], rows past N read as zero
+        const int per_mat = BN * x.kg;  // bytes, a multiple of 16
+        unsigned char* sc = smem + C::SMEM;
+        for (int m = 0; m < C::NMAT; ++m)
+            for (int c = tid * 16; c < per_mat; c += kThreads * 16)
+                *reinterpret_cast<u32x4*>(sc + m * per_mat + c) = buf_load16(x.src.s[m], (uint32_t)(n0 * x.kg + c), 0);
+    } else {
+        const uint32_t wbytes = (uint32_t)((size_t)N * K * 2);
+        x.src.w[0] = make_rsrc((const unsigned char*)args.w0 + (size_t)e * wbytes, wbytes);
+        x.src.w[1] = MODE == 0 ? make_rsrc((const unsigned char*)args.w1 + (size_t)e * wbytes, wbytes) : x.src.w[0];
+        x.src.s[0] = x.src.s[1] = x.src.w[0];
+#pragma unroll
+        for (int i = 0; i < C::B_DMA; ++i) {
+            const int blk = wave + kWaves * i;
+            x.b_mat[i] = (blk * 8) / BN;
+            const int n = min(n0 + (blk * 8) % BN + rb, N - 1);
+            x.b_voff[i] = (uint32_t)n * (uint32_t)K * 2u + (chunk_even ^ (uint32_t)(blk & 1)) * 16u;
+        }
     }
 
     const int nk = K / kBK;
 #pragma unroll
     for (int s = 0; s < C::NST; ++s)
-        if (s < nk) dma_stage<C>(src, smem, s, wave, a_voff, b_voff, b_mat);
+        if (s < nk) dma_stage<C>(x.src, smem, s, wave, x.a_voff, x.b_voff, x.b_mat);
 
     f32x16 acc[C::NMAT][C::MBW][C::NBW];
 #pragma unroll
@@ -336,7 +439,7 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
     // live 32-row groups of this wave: wm + kWM i below ceil(rows / 32)
     const int live32 = (rows + 31) >> 5;
     const int mine = live32 > wm ? (live32 - wm + kWM - 1) / kWM : 0;
-    dispatch_mb<C, BN, C::MBW>(mine, src, smem, nk, wave, lane, a_voff, b_voff, b_mat, acc);
+    dispatch_mb<C, BN, C::MBW>(mine, x, smem, nk, wave, lane, acc);
 
     // ---- epilogue: D[v] of a 32x32 tile is row 8(v/4) + 4(l/32) + v%4, column l%32 ----
     const int fr = lane & 31, fh = lane >> 5;
@@ -373,7 +476,7 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
 // in order from the XCD's counter, so a workgroup that drew cheap items (the
 // short last row tile of an expert) takes more of them, and the row tiles
 // sharing a weight tile still run together on one XCD.
-template <int MODE, int BN, int S>
+template <int MODE, int BN, int S, bool MXW>
 __device__ __forceinline__ void gemm_body(const BArgs& args) {
     __shared__ int s_q;
     const int n_work = args.n_work[0];
@@ -388,16 +491,25 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
         bare_barrier();
         const int q = __builtin_amdgcn_readfirstlane(s_q);
         if (q >= end) break;
-        process_item<MODE, BN, S>(args, q);
+        process_item<MODE, BN, S, MXW>(args, q);
     }
 }
 
-using CfgGateUp = Cfg<0, kBNGateUp, kStagesGateUp>;
-using CfgDown = Cfg<1, kBNDown, kStagesDown>;
+// MXFP4 weights: a quarter of the bytes per stage, so three stages fit beside
+// the tile's scales.
+template <bool MXW>
+using CfgGateUp = Cfg<0, kBNGateUp, MXW ? 3 : kStagesGateUp, MXW>;
+template <bool MXW>
+using CfgDown = Cfg<1, kBNDown, MXW ? 3 : kStagesDown, MXW>;
+
+template <bool MXW>
 __global__ __launch_bounds__(kThreads) void gateup_bf16_kernel(BArgs args) {
-    gemm_body<0, kBNGateUp, kStagesGateUp>(args);
+    gemm_body<0, kBNGateUp, CfgGateUp<MXW>::NST, MXW>(args);
 }
-__global__ __launch_bounds__(kThreads) void down_bf16_kernel(BArgs args) { gemm_body<1, kBNDown, kStagesDown>(args); }
+template <bool MXW>
+__global__ __launch_bounds__(kThreads) void down_bf16_kernel(BArgs args) {
+    gemm_body<1, kBNDown, CfgDown<MXW>::NST, MXW>(args);
+}
 
 BArgs make_args(const GemmProblem& p, int mode) {
     BArgs a{};
@@ -410,6 +522,8 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.a_bytes = (uint32_t)((size_t)p.T * p.H * 2);
         a.w0 = p.w_gate;
         a.w1 = p.w_up;
+        a.s0 = p.s_gate;
+        a.s1 = p.s_up;
         a.out = p.act;
         a.K = p.H;
         a.N = p.I;
@@ -422,6 +536,8 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.a_bytes = (uint32_t)((size_t)p.T * p.k * p.I * 2);
         a.w0 = p.w_down;
         a.w1 = p.w_down;
+        a.s0 = p.s_down;
+        a.s1 = p.s_down;
         a.out = p.y;
         a.K = p.I;
         a.N = p.H;
@@ -459,20 +575,37 @@ hipError_t launch(Kern kern, size_t smem, const BArgs& a, hipStream_t stream) {
 int bf16_block_m() { return kBM; }
 int bf16_col_tiles(int N, int mode) { return (N + (mode == 0 ? kBNGateUp : kBNDown) - 1) / (mode == 0 ? kBNGateUp : kBNDown); }
 
-hipError_t launch_gateup_bf16w(const GemmProblem& p, hipStream_t stream) {
-    constexpr size_t smem = CfgGateUp::SMEM;
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)gateup_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+// Dynamic LDS a workgroup may use: 160 KB less room for the static work-item slot.
+constexpr size_t kMaxLds = 160 * 1024 - 1024;
+
+// Largest contraction depth the MXFP4 kernels take (the tile's scales for all
+// of K sit in LDS beside the ring), a multiple of 64.
+int mxfp4_max_k() {
+    const size_t fixed = CfgGateUp<true>::SMEM > CfgDown<true>::SMEM ? CfgGateUp<true>::SMEM : CfgDown<true>::SMEM;
+    const size_t rows = 2 * kBNGateUp > kBNDown ? 2 * kBNGateUp : kBNDown;
+    return (int)((kMaxLds - fixed) / rows * 32) / 64 * 64;
+}
+
+template <bool MXW, class Kern>
+hipError_t launch_mode(Kern kern, size_t smem, const BArgs& a, hipStream_t stream) {
+    static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)kMaxLds);
     if (attr != hipSuccess) return attr;
-    return launch(gateup_bf16_kernel, smem, make_args(p, 0), stream);
+    return launch(kern, smem, a, stream);
+}
+
+hipError_t launch_gateup_bf16w(const GemmProblem& p, hipStream_t stream) {
+    const BArgs a = make_args(p, 0);
+    if (p.expert_dtype == DT_MXFP4)
+        return launch_mode<true>(gateup_bf16_kernel<true>, CfgGateUp<true>::smem(a.K), a, stream);
+    return launch_mode<false>(gateup_bf16_kernel<false>, CfgGateUp<false>::smem(a.K), a, stream);
 }
 
 hipError_t launch_down_bf16w(const GemmProblem& p, hipStream_t stream) {
-    constexpr size_t smem = CfgDown::SMEM;
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)down_bf16_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (attr != hipSuccess) return attr;
-    return launch(down_bf16_kernel, smem, make_args(p, 1), stream);
+    const BArgs a = make_args(p, 1);
+    if (p.expert_dtype == DT_MXFP4)
+        return launch_mode<true>(down_bf16_kernel<true>, CfgDown<true>::smem(a.K), a, stream);
+    return launch_mode<false>(down_bf16_kernel<false>, CfgDown<false>::smem(a.K), a, stream);
 }
 
 }  // namespace moe

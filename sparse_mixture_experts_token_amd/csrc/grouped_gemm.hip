@@ -1,5 +1,5 @@
 // Stages 2 and 3 of the layer for fp32 activations and weights (the generic
-// path; bf16 activations use the tuned kernels of gemm_prefill.hip): the
+// path; bf16 activations use gemm_bf16.hip and gemm_decode.hip): the
 // experts' SwiGLU networks as two grouped GEMMs over the expert-major row tiles ("gpt-oss 20B" field guide, cutaway 03:
 // SwiGLU experts; "openai/gpt-oss-20b" fixture comparison: hidden_act silu).
 //
@@ -326,30 +326,26 @@ Args make_args(const GemmProblem& p, int mode) {
 
 }  // namespace
 
-int prefill_block_m();
-hipError_t launch_gateup_bf16(const GemmProblem& p, hipStream_t stream);
-hipError_t launch_down_bf16(const GemmProblem& p, hipStream_t stream);
 
 int gemm_block_m(int act_dtype, int expert_dtype, int, int, int) {
     if (act_dtype == DT_F32) return kBM;
-    return expert_dtype == DT_MXFP4 ? prefill_block_m() : bf16_block_m();
+    (void)expert_dtype;
+    return bf16_block_m();
 }
 
 // fp32 activations take the generic kernel; bf16 activations the decode kernels
-// (few rows per expert) or the prefill ones (gemm_bf16.hip for bf16 weights,
-// gemm_prefill.hip for MXFP4 weights).
+// (few rows per expert) or the prefill ones (gemm_bf16.hip, bf16 or MXFP4
+// weights).
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream) {
     if (p.act_dtype == DT_F32) return launch_on<0, float, DT_F32, kBM, kBNGateUp>(make_args(p, 0), stream);
     if (p.decode) return launch_gateup_decode(p, stream);
-    if (p.expert_dtype == DT_BF16) return launch_gateup_bf16w(p, stream);
-    return launch_gateup_bf16(p, stream);
+    return launch_gateup_bf16w(p, stream);
 }
 
 hipError_t launch_down(const GemmProblem& p, hipStream_t stream) {
     if (p.act_dtype == DT_F32) return launch_on<1, float, DT_F32, kBM, kBNDown>(make_args(p, 1), stream);
     if (p.decode) return launch_down_decode(p, stream);
-    if (p.expert_dtype == DT_BF16) return launch_down_bf16w(p, stream);
-    return launch_down_bf16(p, stream);
+    return launch_down_bf16w(p, stream);
 }
 
 }  // namespace moe

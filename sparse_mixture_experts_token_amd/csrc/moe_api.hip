@@ -27,6 +27,8 @@ int check_problem(const moe_problem* p) {
     const int64_t big = (int64_t)p->T * p->k * (p->H > p->I ? p->H : p->I);
     if (big >= (int64_t(1) << 31)) return MOE_ERR_SHAPE;
     if ((int64_t)p->H * p->I >= (int64_t(1) << 29)) return MOE_ERR_SHAPE;
+    // MXFP4: a GEMM tile keeps its scales for the whole contraction in LDS
+    if (p->expert_dtype == MOE_MXFP4 && (p->H > moe::mxfp4_max_k() || p->I > moe::mxfp4_max_k())) return MOE_ERR_SHAPE;
     const bool ok = (p->act_dtype == MOE_F32 && p->expert_dtype == MOE_F32) ||
                     (p->act_dtype == MOE_BF16 && (p->expert_dtype == MOE_BF16 || p->expert_dtype == MOE_MXFP4));
     if (!ok) return MOE_ERR_DTYPE;
@@ -38,6 +40,7 @@ struct Layout {
     size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, queues, work0, work1, act, y, total;
     int nblk, max_tiles, BM, nc0, nc1;
     bool decode;
+    bool lists;  // prefill work lists are built
 };
 
 Layout layout(const moe_problem* p) {
@@ -59,9 +62,10 @@ Layout layout(const moe_problem* p) {
     L.ntiles = o;   o = align_up(o + 16);  // tile count, then the two work-list counts
     L.queues = o;   o = align_up(o + moe::kNumQueues * 4);
     // column tiles of the prefill work lists (the decode kernels need none)
-    const bool bf16w = p->act_dtype == MOE_BF16 && p->expert_dtype == MOE_BF16;
-    L.nc0 = L.decode ? 0 : bf16w ? moe::bf16_col_tiles(p->I, 0) : moe::prefill_col_tiles(p->I, 0);
-    L.nc1 = L.decode ? 0 : bf16w ? moe::bf16_col_tiles(p->H, 1) : moe::prefill_col_tiles(p->H, 1);
+    // (only the bf16-activation prefill kernels walk work lists)
+    L.lists = !L.decode && p->act_dtype == MOE_BF16;
+    L.nc0 = L.lists ? moe::bf16_col_tiles(p->I, 0) : 0;
+    L.nc1 = L.lists ? moe::bf16_col_tiles(p->H, 1) : 0;
     L.work0 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc0 * 4);
     L.work1 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc1 * 4);
     L.act = o;      o = align_up(o + tk * p->I * act_bytes(p->act_dtype));
@@ -170,8 +174,8 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
                            topk_w, blk, rank, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(1);
-    moe::WorkList wl0{L.decode ? nullptr : (int32_t*)(ws + L.work0), ntiles + 1, L.nc0};
-    moe::WorkList wl1{L.decode ? nullptr : (int32_t*)(ws + L.work1), ntiles + 2, L.nc1};
+    moe::WorkList wl0{L.lists ? (int32_t*)(ws + L.work0) : nullptr, ntiles + 1, L.nc0};
+    moe::WorkList wl1{L.lists ? (int32_t*)(ws + L.work1) : nullptr, ntiles + 2, L.nc1};
     int32_t* queues = (int32_t*)(ws + L.queues);
     e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
                                L.max_tiles, wl0, wl1, queues, moe::kNumQueues, stream);

@@ -202,7 +202,7 @@ bool decode_path(int act_dtype, int T, int H, int I, int E, int k);
 int decode_block_m();
 hipError_t launch_gateup_decode(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down_decode(const GemmProblem& p, hipStream_t stream);
-int prefill_col_tiles(int N, int mode);  // column tiles of the bf16 GEMMs (mode 0 gate/up, 1 down)
+int mxfp4_max_k();                   // largest H or I the MXFP4 kernels take
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, hipStream_t stream);
 
