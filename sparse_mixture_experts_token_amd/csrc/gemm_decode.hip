@@ -1,45 +1,61 @@
-// Stages 2 and 3 for decode-sized batches (few rows per expert): the same two
-// grouped products as the prefill kernels,
+// The layer for decode-sized batches (few rows per expert), organised for the
+// case where it is bound by reading the experts' weights once from HBM rather
+// than by the matrix cores.  The two grouped products are those of the
+// prefill kernels,
 //
 //   act[r]  = silu(W_gate[e] . x_r) * (W_up[e] . x_r)       x_r = h[perm_src[r] / k]
 //   Y[a]    = p_a * (W_down[e] . act[r])                     a = perm_src[r]
 //
 // ("gpt-oss-40b-64a8-init" page, section 2, Proof; "gpt-oss 20B" field guide,
-// cutaway 03: SwiGLU experts), organised for the case where they are bound by
-// reading the experts' weights once from HBM rather than by the matrix cores.
+// cutaway 03: SwiGLU experts).
 //
-// One wave computes one (row tile of at most 16 rows of one expert) x (16
-// weight rows) block with 16x16x32 bf16 MFMAs: the weights are the A operand,
-// streamed from HBM straight into registers (no LDS, no barriers), the
-// tile's activation rows are the B operand (small, L2-resident).  Lanes of
-// rows past the tile's end read at an offset beyond the buffer, which returns
-// zero without touching memory.
+// Products.  One wave computes one (row tile of at most 16 rows of one expert)
+// x (up to 32 weight rows) block with 16x16x32 bf16 MFMAs: the weights are
+// the A operand, streamed from HBM straight into registers (no LDS, no
+// barriers), the tile's activation rows are the B operand (small,
+// L2-resident).  Lanes of rows past the tile's end, and weight rows past the
+// end of a block, read at an offset beyond the buffer, which returns zero
+// without touching memory.
 //
 // K is walked 128 at a time, as four 32-deep MFMA steps j.  For bf16 weights
 // each load instruction takes the native MFMA order (lane (row l%16, quarter
 // q = l/16) reads K elements 128g + 32j + 8q .. +7), so one instruction reads
-// 64 contiguous bytes of each of 16 weight rows.  For MXFP4 a lane reads the
-// 32 codes [128g + 32q, 128g + 32q + 32) of its row in one 16-byte load plus
-// exactly one E8M0 scale, and feeds them to the four steps as elements
-// 8j..8j+7; a contraction is unchanged by a permutation of K applied to both
-// operands, so the activation operand is read in the same permuted order.
+// 64 contiguous bytes of each of 16 weight rows; at this size every
+// per-instruction row segment from 64 to 256 bytes streams at the same rate.
+// For MXFP4 a lane reads the 32 codes [128g + 32q, 128g + 32q + 32) of its
+// row in one 16-byte load plus exactly one E8M0 scale, and feeds them to the
+// four steps as elements 8j..8j+7; a contraction is unchanged by a
+// permutation of K applied to both operands, so the activation operand is
+// read in the same permuted order.  All loads of a K step are issued before
+// its MFMAs (scheduling barriers keep the compiler from interleaving them,
+// which would leave only a few loads in flight); the down product also keeps
+// the next step's loads in flight while multiplying.
 //
-// Each wave owns two 16-row weight panels (32 weight rows), sharing every
-// activation fragment between them (and between gate and up), and the down
-// kernel issues the loads of two K steps before their MFMAs: together this
-// keeps enough bytes in flight per CU for HBM while every work item of a
-// decode-sized batch is resident at once.  Consecutive waves take consecutive
-// panels of the same row tile, so a workgroup streams one contiguous weight
-// region and shares the tile's activation rows in L1.
+// Work split.  Gate/up runs with one workgroup per CU: the (tile, weight row)
+// pairs are split into equal contiguous ranges, one per workgroup, and each
+// range into equal sub-ranges, one per wave, with boundaries on multiples of
+// four rows; a wave walks its sub-range in passes of at most 32 rows.  Down
+// (half the bytes) runs one 32-row block per wave.
+//
+// Fused routing.  When the batch and the router are small (T <= 64, E <= 64)
+// a small kernel writes partial router logits (K split into slices), and
+// every gate/up workgroup then completes the routing of the batch itself -
+// logits, top-k, softmax over the selected set, the stable expert-major order
+// and the tile list - in its LDS; workgroup 0 also writes it out for the down
+// product and the caller.  Redundant, but a few microseconds of work on data
+// in L2 instead of the router's and the route scan's dependent launches.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kDecWaves = 4;           // waves per workgroup (independent)
 constexpr int kDecRows = 16;           // rows per tile (MFMA N)
-constexpr int kPanels = 2;             // 16-row weight panels per wave
-constexpr int kDecCols = 16 * kPanels; // weight rows per wave
+constexpr int kPanels = 2;             // 16-row weight panels per pass
+constexpr int kDecCols = 16 * kPanels; // weight rows per pass
+constexpr int kRowAlign = 4;           // range boundaries: whole 8-/16-byte output stores
+constexpr int kGuWaves = 12;           // gate/up: waves per workgroup, one workgroup per CU
+constexpr int kDnWaves = 4;            // down: waves per workgroup, one 32-row block per wave
+constexpr int kMinLds = 96 * 1024;     // LDS per gate/up workgroup: room for no second one on the CU
 constexpr uint32_t kOob = 0x7ffffff0u; // byte offset past every buffer used here (all < 2^30 bytes)
 
 struct DArgs {
@@ -54,52 +70,10 @@ struct DArgs {
     const Tile* tiles;
     const int32_t* n_tiles;
     void* out;          // act [T*k][N] bf16 (gate/up) or Y [T*k][N] f32 (down)
-    int K, N, k, n_cb;  // n_cb = N / 32
+    int K, N, k, max_tiles;
 };
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.f + __expf(-x)); }
-
-// Raw weight data of one 128-wide K step for this lane (decoded at use).
-template <int WDT>
-struct WRaw {
-    u32x4 v[4];
-};
-template <>
-struct WRaw<DT_MXFP4> {
-    u32x4 q;
-    uint32_t scale;
-};
-
-template <int WDT>
-__device__ __forceinline__ void load_w(buf_rsrc w, buf_rsrc s, uint32_t n, uint32_t K, uint32_t g, uint32_t qd,
-                                       WRaw<WDT>& o) {
-    if constexpr (WDT == DT_MXFP4) {
-        const uint32_t kq = g * 128 + qd * 32;
-        const bool kv = kq < K;
-        o.q = buf_load16(w, kv ? n * (K / 2) + kq / 2 : kOob, 0);
-        o.scale = buf_load1(s, kv ? n * (K / 32) + kq / 32 : kOob, 0);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t kk = g * 128 + 32 * j + 8 * qd;
-            o.v[j] = buf_load16(w, kk < K ? (n * K + kk) * 2u : kOob, 0);
-        }
-    }
-}
-
-template <int WDT>
-__device__ __forceinline__ void w_frags(const WRaw<WDT>& o, bf16x8 (&f)[4]) {
-    if constexpr (WDT == DT_MXFP4) {
-        uint32_t d[16];
-        decode_mxfp4_32(o.q, o.scale, d);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            f[j] = __builtin_bit_cast(bf16x8, u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f[j] = __builtin_bit_cast(bf16x8, o.v[j]);
-    }
-}
 
 // Activation fragments of one K step, in the K order of the weights.
 template <int WDT>
@@ -112,14 +86,94 @@ __device__ __forceinline__ void load_b(buf_rsrc b, uint32_t b_base, bool has_row
     }
 }
 
+// The loads of one 128-wide K step, in flat register arrays (weights of
+// panel p: wq[4p..4p+3] for bf16, wq[p] + ws[p] for MXFP4; up weights in
+// uq / us; activations in b).
 template <int MODE, int WDT>
-__global__ __launch_bounds__(kDecWaves * 64) void decode_gemm_kernel(DArgs a) {
-    constexpr int G = MODE == 0 ? 1 : 2;  // K steps whose loads are issued together
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int q = blockIdx.x * kDecWaves + wave;
-    const int mt = q / a.n_cb, cb = q % a.n_cb;
-    if (mt >= a.n_tiles[0]) return;  // wave-uniform; this kernel has no barriers
-    const Tile tile = a.tiles[mt];
+struct Batch {
+    static constexpr int NQ = WDT == DT_MXFP4 ? kPanels : 4 * kPanels;
+    u32x4 wq[NQ];
+    u32x4 uq[MODE == 0 ? NQ : 1];
+    uint32_t ws[kPanels];
+    uint32_t us[kPanels];
+    u32x4 b[4];
+};
+
+template <int MODE, int WDT>
+__device__ __forceinline__ void issue(Batch<MODE, WDT>& x, buf_rsrc w0, buf_rsrc w1, buf_rsrc s0, buf_rsrc s1,
+                                      buf_rsrc bsrc, const uint32_t (&n)[kPanels], const bool (&nv)[kPanels],
+                                      uint32_t b_base, bool has_row, uint32_t K, uint32_t g, uint32_t qd) {
+#pragma unroll
+    for (int p = 0; p < kPanels; ++p) {
+        if constexpr (WDT == DT_MXFP4) {
+            const uint32_t kq = g * 128 + qd * 32;
+            const bool kv = nv[p] && kq < K;
+            const uint32_t co = kv ? n[p] * (K / 2) + kq / 2 : kOob, so = kv ? n[p] * (K / 32) + kq / 32 : kOob;
+            x.wq[p] = buf_load16(w0, co, 0);
+            x.ws[p] = buf_load1(s0, so, 0);
+            if constexpr (MODE == 0) {
+                x.uq[p] = buf_load16(w1, co, 0);
+                x.us[p] = buf_load1(s1, so, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t kk = g * 128 + 32 * j + 8 * qd;
+                const uint32_t o = (nv[p] && kk < K) ? (n[p] * K + kk) * 2u : kOob;
+                x.wq[4 * p + j] = buf_load16(w0, o, 0);
+                if constexpr (MODE == 0) x.uq[4 * p + j] = buf_load16(w1, o, 0);
+            }
+        }
+    }
+    load_b<WDT>(bsrc, b_base, has_row, K, g, qd, x.b);
+}
+
+template <int WDT, int NQ>
+__device__ __forceinline__ void frags(const u32x4 (&q)[NQ], uint32_t scale, int p, bf16x8 (&f)[4]) {
+    uint32_t d[16];
+    decode_mxfp4_32(q[p], scale, d);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        f[j] = __builtin_bit_cast(bf16x8, u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
+}
+
+template <int MODE, int WDT>
+__device__ __forceinline__ void compute(const Batch<MODE, WDT>& x, f32x4 (&acc0)[kPanels], f32x4 (&acc1)[kPanels]) {
+    if constexpr (WDT != DT_MXFP4) {
+        // each 16-byte register straight into its MFMA (no fragment copies,
+        // which would keep the batch in scratch memory)
+#pragma unroll
+        for (int p = 0; p < kPanels; ++p)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bf16x8 bj = __builtin_bit_cast(bf16x8, x.b[j]);
+                acc0[p] = mfma16(__builtin_bit_cast(bf16x8, x.wq[4 * p + j]), bj, acc0[p]);
+                if constexpr (MODE == 0) acc1[p] = mfma16(__builtin_bit_cast(bf16x8, x.uq[4 * p + j]), bj, acc1[p]);
+            }
+    } else {
+#pragma unroll
+        for (int p = 0; p < kPanels; ++p) {
+            bf16x8 fa[4];
+            frags<WDT>(x.wq, x.ws[p], p, fa);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc0[p] = mfma16(fa[j], __builtin_bit_cast(bf16x8, x.b[j]), acc0[p]);
+            if constexpr (MODE == 0) {
+                bf16x8 fu[4];
+                frags<WDT>(x.uq, x.us[p], p, fu);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc1[p] = mfma16(fu[j], __builtin_bit_cast(bf16x8, x.b[j]), acc1[p]);
+            }
+        }
+    }
+}
+
+// One block: weight rows [c0, c1) (c1 - c0 <= 32, both multiples of four) of
+// the expert of `tile` against the tile's activation rows; perm holds the
+// assignment of every expert-major row (global memory or LDS).  DEPTH = K
+// steps of loads in flight (1 or 2).
+template <int MODE, int WDT, int DEPTH>
+__device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, const int32_t* perm, uint32_t c0,
+                                            uint32_t c1, int lane) {
     const int e = tile.expert, row0 = tile.row_start, rows = tile.rows;
     const uint32_t K = (uint32_t)a.K, N = (uint32_t)a.N;
     const int r = lane & 15;
@@ -129,15 +183,19 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gemm_kernel(DArgs a) {
     const bool has_row = r < rows;
     uint32_t b_base = 0;
     if (has_row) {
-        const int src = MODE == 0 ? a.perm_src[row0 + r] / a.k : row0 + r;
+        const int src = MODE == 0 ? perm[row0 + r] / a.k : row0 + r;
         b_base = (uint32_t)src * K * 2u;
     }
     const buf_rsrc bsrc = make_rsrc(a.a_src, a.a_bytes);
 
-    // weight operand: rows n[p] of expert e
+    // weight operand: rows n[p] of expert e, present while below c1
     uint32_t n[kPanels];
+    bool nv[kPanels];
 #pragma unroll
-    for (int p = 0; p < kPanels; ++p) n[p] = (uint32_t)(cb * kDecCols + p * 16 + r);
+    for (int p = 0; p < kPanels; ++p) {
+        n[p] = c0 + (uint32_t)(p * 16 + r);
+        nv[p] = n[p] < c1;
+    }
     buf_rsrc w0, w1, s0, s1;
     if constexpr (WDT == DT_MXFP4) {
         const uint32_t wb = N * K / 2, sb = N * K / 32;
@@ -155,62 +213,331 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gemm_kernel(DArgs a) {
     f32x4 acc0[kPanels], acc1[kPanels];
 #pragma unroll
     for (int p = 0; p < kPanels; ++p) acc0[p] = acc1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Steps past the end read beyond K: zeros, no memory traffic.
     const uint32_t ng = (K + 127) / 128;
-    for (uint32_t g0 = 0; g0 < ng; g0 += G) {
-        WRaw<WDT> ra[G][kPanels], ru[G][kPanels];
-        u32x4 fb[G][4];
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg) {
-            const uint32_t g = g0 + gg;  // past the end: every offset is beyond K, so all zero
-#pragma unroll
-            for (int p = 0; p < kPanels; ++p) {
-                load_w<WDT>(w0, s0, n[p], K, g, qd, ra[gg][p]);
-                if constexpr (MODE == 0) load_w<WDT>(w1, s1, n[p], K, g, qd, ru[gg][p]);
-            }
-            load_b<WDT>(bsrc, b_base, has_row, K, g, qd, fb[gg]);
+    Batch<MODE, WDT> x0, x1;
+    if constexpr (DEPTH == 1) {
+        for (uint32_t g = 0; g < ng; ++g) {
+            issue<MODE, WDT>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g, qd);
+            __builtin_amdgcn_sched_barrier(0);
+            compute<MODE, WDT>(x0, acc0, acc1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg) {
-#pragma unroll
-            for (int p = 0; p < kPanels; ++p) {
-                bf16x8 fa[4];
-                w_frags<WDT>(ra[gg][p], fa);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc0[p] = mfma16(fa[j], __builtin_bit_cast(bf16x8, fb[gg][j]), acc0[p]);
-                if constexpr (MODE == 0) {
-                    bf16x8 fu[4];
-                    w_frags<WDT>(ru[gg][p], fu);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc1[p] = mfma16(fu[j], __builtin_bit_cast(bf16x8, fb[gg][j]), acc1[p]);
-                }
-            }
+    } else {
+        issue<MODE, WDT>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, 0, qd);
+        for (uint32_t g = 0; g < ng; g += 2) {
+            issue<MODE, WDT>(x1, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 1, qd);
+            __builtin_amdgcn_sched_barrier(0);
+            compute<MODE, WDT>(x0, acc0, acc1);
+            __builtin_amdgcn_sched_barrier(0);
+            issue<MODE, WDT>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 2, qd);
+            __builtin_amdgcn_sched_barrier(0);
+            compute<MODE, WDT>(x1, acc0, acc1);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
-    // D: lane l holds weight rows 4(l/16)+i (i = 0..3) of the panel, for row l%16 of the tile
+    // D: lane l holds weight rows 4(l/16)+i (i = 0..3) of the panel, for row l%16
+    // of the tile; c0 and c1 are multiples of four, so those four rows are all
+    // present or all absent.
     if (!has_row) return;
     if constexpr (MODE == 0) {
         uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (size_t)(row0 + r) * N;
 #pragma unroll
         for (int p = 0; p < kPanels; ++p) {
-            const uint32_t n0 = (uint32_t)(cb * kDecCols + p * 16) + 4 * qd;
+            const uint32_t n0 = c0 + (uint32_t)(p * 16) + 4 * qd;
+            if (n0 >= c1) continue;
             uint32_t v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16_bits(silu_f(acc0[p][i]) * acc1[p][i]);
             *reinterpret_cast<uint2*>(orow + n0) = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
         }
     } else {
-        const int asg = a.perm_src[row0 + r];
+        const int asg = perm[row0 + r];
         const float pw = a.topk_w[asg];
         float* orow = reinterpret_cast<float*>(a.out) + (size_t)asg * N;
 #pragma unroll
         for (int p = 0; p < kPanels; ++p) {
-            const uint32_t n0 = (uint32_t)(cb * kDecCols + p * 16) + 4 * qd;
+            const uint32_t n0 = c0 + (uint32_t)(p * 16) + 4 * qd;
+            if (n0 >= c1) continue;
             *reinterpret_cast<float4*>(orow + n0) =
                 float4{acc0[p][0] * pw, acc0[p][1] * pw, acc0[p][2] * pw, acc0[p][3] * pw};
         }
     }
+}
+
+// This wave's equal share of the (tile, weight row) pairs, tile-major, in
+// units of kRowAlign rows: workgroups take equal contiguous ranges and their
+// W waves equal sub-ranges.
+template <int MODE, int WDT, int DEPTH, int W>
+__device__ __forceinline__ void balanced_share(const DArgs& a, const Tile* tiles, const int32_t* perm, int ntl,
+                                               int wave, int lane) {
+    const int64_t upt = a.N / kRowAlign;  // units per tile
+    const int64_t units = (int64_t)ntl * upt;
+    const int64_t g = gridDim.x, b = blockIdx.x;
+    const int64_t b_lo = units * b / g, b_hi = units * (b + 1) / g;
+    const int64_t w_lo = b_lo + (b_hi - b_lo) * wave / W;
+    const int64_t w_hi = b_lo + (b_hi - b_lo) * (wave + 1) / W;
+    for (int64_t u = w_lo; u < w_hi;) {
+        const int mt = (int)(u / upt);
+        const int64_t s_lo = u - mt * upt;
+        const int64_t s_hi = min(upt, s_lo + (w_hi - u));
+        const uint32_t r_hi = (uint32_t)(s_hi * kRowAlign);
+        const Tile tile = tiles[mt];
+        for (uint32_t c = (uint32_t)(s_lo * kRowAlign); c < r_hi; c += kDecCols)
+            decode_pass<MODE, WDT, DEPTH>(a, tile, perm, c, min(r_hi, c + (uint32_t)kDecCols), lane);
+        u += s_hi - s_lo;
+    }
+}
+
+// Gate/up over the tile list written by the route scan.
+template <int WDT>
+__global__ __launch_bounds__(kGuWaves * 64) void decode_gateup_kernel(DArgs a) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int ntl = min(a.n_tiles[0], a.max_tiles);
+    balanced_share<0, WDT, 1, kGuWaves>(a, a.tiles, a.perm_src, ntl, wave, lane);
+}
+
+// Down: wave q takes 32-row block q % (N/32) of tile q / (N/32).
+template <int WDT>
+__global__ __launch_bounds__(kDnWaves * 64) void decode_down_kernel(DArgs a) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int ntl = min(a.n_tiles[0], a.max_tiles);
+    const int ncb = a.N / kDecCols;
+    const int q = blockIdx.x * kDnWaves + wave;
+    const int mt = q / ncb, cb = q - mt * ncb;
+    if (mt >= ntl) return;  // wave-uniform; this kernel has no barriers
+    decode_pass<1, WDT, 2>(a, a.tiles[mt], a.perm_src, (uint32_t)(cb * kDecCols), (uint32_t)((cb + 1) * kDecCols),
+                           lane);
+}
+
+// ------------------------------------------------ fused routing + gate/up --
+//
+//   s_t,i = W_r[i] . h_t + b_r[i]          fp32, from bf16 MFMA tiles
+//   S_t   = the k largest s_t,i            ties (and NaN, which ranks last) to the lower index
+//   p_t,i = exp(s_t,i - max S_t) / sum_{j in S_t} exp(s_t,j - max S_t)
+//
+// ("gpt-oss-40b-64a8-init" page, section 2, Proof.)  The logits kernel splits
+// the K range into kLogitSlices interleaved slices and writes one partial sum
+// per (slice, token, expert) from a 16x16 MFMA tile per wave; the fused
+// kernel adds the slices in slice order and then the bias, so every expert
+// column goes through exactly the same operations (identical router rows give
+// identical logits).
+//
+// Top-k by rank: each logit gets a 64-bit order key - its value mapped to an
+// order-preserving unsigned integer (NaN lowest, -0 as +0) above the
+// complement of its expert index - so "a beats b" (larger value, ties to the
+// lower index) is one integer comparison, and the lane of expert e is
+// selected when fewer than k keys exceed its own.  The expert-major order is
+// a stable counting sort by token: with T <= 64 each expert keeps the set of
+// its tokens as a 64-bit mask, and a row's place among the expert's rows is
+// the number of earlier tokens in that mask.
+
+constexpr int kFMaxT = 64;        // tokens (one bit each in a 64-bit mask)
+constexpr int kFMaxE = 64;        // experts (one per lane in top-k)
+constexpr int kLogitSlices = 8;   // K slices of the partial logits
+constexpr int kLogitSteps = 12;   // 32-wide K steps per batch of loads in the logits kernel
+
+// Partial logits: block (ks, tile) computes token tile tile / ET x expert
+// tile tile % ET over the K steps s = ks (mod kLogitSlices).
+__global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __restrict__ h,
+                                                           const uint16_t* __restrict__ wr, int T, int E, int H,
+                                                           float* __restrict__ part) {
+    const int lane = threadIdx.x;
+    const int ET = (E + 15) / 16;
+    const int ks = blockIdx.x, tt = blockIdx.y / ET, et = blockIdx.y - (blockIdx.y / ET) * ET;
+    const int r = lane & 15, koff = (lane >> 4) * 8;
+    const uint16_t* hrow = h + (size_t)min(tt * 16 + r, T - 1) * H;
+    const uint16_t* wrow = wr + (size_t)min(et * 16 + r, E - 1) * H;
+    const int nsteps = H / 32;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = ks; s0 < nsteps; s0 += kLogitSlices * kLogitSteps) {
+        bf16x8 av[kLogitSteps], bv[kLogitSteps];
+#pragma unroll
+        for (int q = 0; q < kLogitSteps; ++q) {
+            const int s = s0 + q * kLogitSlices;
+            const int kk = (s < nsteps ? s : ks) * 32 + koff;  // past the end: a valid step, discarded
+            av[q] = *reinterpret_cast<const bf16x8*>(hrow + kk);
+            bv[q] = *reinterpret_cast<const bf16x8*>(wrow + kk);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the whole batch of loads ahead of the MFMAs
+#pragma unroll
+        for (int q = 0; q < kLogitSteps; ++q)
+            if (s0 + q * kLogitSlices < nsteps) acc = mfma16(av[q], bv[q], acc);
+    }
+    // D[j]: token 4(l/16)+j of the token tile, expert l%16 of the expert tile
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = tt * 16 + (lane >> 4) * 4 + j, e = et * 16 + r;
+        if (t < T && e < E) part[((size_t)ks * T + t) * E + e] = acc[j];
+    }
+}
+
+struct FArgs {
+    DArgs g;            // the gate/up product (tiles and perm_src are taken from LDS)
+    const float* part;  // partial logits [kLogitSlices][T][E]
+    const uint16_t* br; // router bias [E] bf16, or null
+    int T, E;
+    float* logits;      // [T][E] or null
+    int32_t* topk_idx;  // [T*k]
+    float* topk_w;      // [T*k]
+    int32_t* offsets;   // [E+1]
+    int32_t* perm_src;  // [T*k]
+    int32_t* inv;       // [T*k]
+    Tile* tiles;        // [max_tiles]
+    int32_t* n_tiles;   // [1]
+};
+
+// LDS layout of the fused kernel (byte offsets), identical on host and device.
+struct FLayout {
+    uint32_t sl, key, mask, off, toff, ti, perm, tiles, total;
+};
+__host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
+__host__ __device__ inline FLayout flayout(int T, int k, int max_tiles) {
+    FLayout L{};
+    uint32_t o = 0;
+    L.sl = o;    o += align16((uint32_t)T * kFMaxE * 4);  // logits [T][64]
+    L.key = o;   o += align16((uint32_t)T * kFMaxE * 8);  // order keys [T][64], 0 past E
+    L.mask = o;  o += align16(kFMaxE * 8);                // tokens of each expert
+    L.off = o;   o += align16((kFMaxE + 1) * 4);
+    L.toff = o;  o += align16((kFMaxE + 1) * 4);
+    L.ti = o;    o += align16((uint32_t)T * k * 4);       // selected expert of each assignment
+    L.perm = o;  o += align16((uint32_t)T * k * 4);       // assignment of each expert-major row
+    L.tiles = o; o += align16((uint32_t)max_tiles * sizeof(Tile));
+    L.total = o;
+    return L;
+}
+
+// Larger value first (NaN last, -0 as +0), then the lower expert index.
+__device__ __forceinline__ unsigned long long order_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    u = (v != v) ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+    return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
+}
+
+template <int WDT>
+__global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArgs f) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const DArgs& a = f.g;
+    const int T = f.T, E = f.E, k = a.k;
+    const FLayout L = flayout(T, k, a.max_tiles);
+    float* sl = reinterpret_cast<float*>(smem + L.sl);
+    unsigned long long* skey = reinterpret_cast<unsigned long long*>(smem + L.key);
+    unsigned long long* emask = reinterpret_cast<unsigned long long*>(smem + L.mask);
+    int32_t* off = reinterpret_cast<int32_t*>(smem + L.off);
+    int32_t* toff = reinterpret_cast<int32_t*>(smem + L.toff);
+    int32_t* ti = reinterpret_cast<int32_t*>(smem + L.ti);
+    int32_t* perm = reinterpret_cast<int32_t*>(smem + L.perm);
+    Tile* tl = reinterpret_cast<Tile*>(smem + L.tiles);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool writer = blockIdx.x == 0;
+
+    // 1. logits = slices added in slice order, then the bias; their order keys
+    if (tid < kFMaxE) emask[tid] = 0ull;
+    for (int i = tid; i < T * kFMaxE; i += kGuWaves * 64) {
+        const int t = i / kFMaxE, e = i - t * kFMaxE;
+        unsigned long long key = 0ull;  // past E: below every key
+        if (e < E) {
+            float v = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < kLogitSlices; ++ks) v += f.part[((size_t)ks * T + t) * E + e];
+            if (f.br) v += bf16_bits_to_f32(f.br[e]);
+            sl[i] = v;
+            key = order_key(v, e);
+            if (writer && f.logits) f.logits[(size_t)t * E + e] = v;
+        }
+        skey[i] = key;
+    }
+    __syncthreads();
+
+    // 2. top-k by rank + softmax over the selected set, one token per wave
+    for (int t = wave; t < T; t += kGuWaves) {
+        const bool ok = lane < E;
+        const unsigned long long mine = skey[t * kFMaxE + lane];
+        const float v = sl[t * kFMaxE + lane];
+        int rank = 0;
+        const u32x4* krow = reinterpret_cast<const u32x4*>(skey + t * kFMaxE);
+#pragma unroll
+        for (int c = 0; c < kFMaxE / 2; ++c) {  // two keys per 16-byte read
+            const u32x4 q = krow[c];
+            const unsigned long long k0 = ((unsigned long long)q.y << 32) | q.x;
+            const unsigned long long k1 = ((unsigned long long)q.w << 32) | q.z;
+            rank += (k0 > mine ? 1 : 0) + (k1 > mine ? 1 : 0);
+        }
+        const bool chosen = ok & (rank < k);
+        const uint64_t top = __ballot(ok & (rank == 0));
+        const float smax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__builtin_ctzll(top)));
+        const float z = chosen ? expf(v - smax) : 0.f;
+        float zs = z;  // butterfly sum: every lane adds the same pairs, so all get the same value
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) zs += __shfl_xor(zs, d, 64);
+        const uint64_t bal = __ballot(chosen);
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const int pos = __popcll(bal & lt);  // ascending expert order
+        if (chosen) {
+            ti[t * k + pos] = lane;
+            atomicOr(&emask[lane], 1ull << t);
+            if (writer) {
+                f.topk_idx[(size_t)t * k + pos] = lane;
+                f.topk_w[(size_t)t * k + pos] = z / zs;
+            }
+        }
+    }
+    __syncthreads();
+
+    // 3. counts, offsets and the tile list (wave 0), then every row's place
+    if (wave == 0) {
+        const int c = lane < E ? __popcll(emask[lane]) : 0;
+        const int nt = (c + kDecRows - 1) / kDecRows;
+        int xs = c, xt = nt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int ys = __shfl_up(xs, d, 64), yt = __shfl_up(xt, d, 64);
+            if (lane >= d) {
+                xs += ys;
+                xt += yt;
+            }
+        }
+        const int o = xs - c, base = xt - nt;
+        if (lane < E) {
+            off[lane] = o;
+            toff[lane] = base;
+            for (int j = 0; j < nt; ++j) {
+                Tile x;
+                x.expert = lane;
+                x.row_start = o + j * kDecRows;
+                x.rows = min(kDecRows, c - j * kDecRows);
+                x.pad = 0;
+                tl[base + j] = x;
+                if (writer) f.tiles[base + j] = x;
+            }
+            if (writer) f.offsets[lane] = o;
+        }
+        if (lane == 63) {
+            off[E] = xs;
+            toff[E] = xt;
+            if (writer) {
+                f.offsets[E] = xs;
+                f.n_tiles[0] = xt;
+            }
+        }
+    }
+    __syncthreads();
+    for (int as = tid; as < T * k; as += kGuWaves * 64) {
+        const int t = as / k, e = ti[as];
+        const int row = off[e] + __popcll(emask[e] & ((1ull << t) - 1ull));
+        perm[row] = as;
+        if (writer) {
+            f.perm_src[row] = as;
+            f.inv[as] = row;
+        }
+    }
+    __syncthreads();
+
+    // 4. gate/up: this workgroup's share of the tiles
+    balanced_share<0, WDT, 1, kGuWaves>(a, tl, perm, min(toff[E], a.max_tiles), wave, lane);
 }
 
 DArgs make_dargs(const GemmProblem& p, int mode) {
@@ -239,16 +566,71 @@ DArgs make_dargs(const GemmProblem& p, int mode) {
         a.K = p.I;
         a.N = p.H;
     }
-    a.n_cb = a.N / kDecCols;  // N is a multiple of 64
+    a.max_tiles = p.max_tiles;  // N is a multiple of kRowAlign and of kDecCols (of 64)
     return a;
 }
 
-template <int MODE, int WDT>
-hipError_t launch_dec(const GemmProblem& p, hipStream_t stream) {
-    const DArgs a = make_dargs(p, MODE);
-    const size_t waves = (size_t)p.max_tiles * a.n_cb;
-    const int blocks = (int)((waves + kDecWaves - 1) / kDecWaves);
-    decode_gemm_kernel<MODE, WDT><<<blocks, kDecWaves * 64, 0, stream>>>(a);
+int cu_count() {
+    static const int cus = [] {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        return n;
+    }();
+    return cus;
+}
+
+constexpr int kMaxLds = 160 * 1024;
+
+template <typename Kern>
+hipError_t allow_lds(Kern kern) {
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - 1024);
+    return attr;
+}
+
+template <int WDT>
+hipError_t launch_gu(const GemmProblem& p, hipStream_t stream) {
+    const DArgs a = make_dargs(p, 0);
+    auto kern = decode_gateup_kernel<WDT>;
+    const hipError_t attr = allow_lds(kern);
+    if (attr != hipSuccess) return attr;
+    kern<<<cu_count(), kGuWaves * 64, kMinLds, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int WDT>
+hipError_t launch_dn(const GemmProblem& p, hipStream_t stream) {
+    const DArgs a = make_dargs(p, 1);
+    const int blocks = (int)(((size_t)p.max_tiles * (a.N / kDecCols) + kDnWaves - 1) / kDnWaves);
+    decode_down_kernel<WDT><<<blocks, kDnWaves * 64, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+template <int WDT>
+hipError_t launch_fused(const GemmProblem& p, const FusedRouting& r, hipStream_t stream) {
+    FArgs f{};
+    f.g = make_dargs(p, 0);
+    f.part = r.part;
+    f.br = reinterpret_cast<const uint16_t*>(r.b_router);
+    f.T = p.T;
+    f.E = p.E;
+    f.logits = r.logits;
+    f.topk_idx = r.topk_idx;
+    f.topk_w = r.topk_w;
+    f.offsets = r.offsets;
+    f.perm_src = r.perm_src;
+    f.inv = r.inv;
+    f.tiles = r.tiles;
+    f.n_tiles = r.n_tiles;
+    const FLayout L = flayout(p.T, p.k, p.max_tiles);
+    const uint32_t smem = L.total > (uint32_t)kMinLds ? L.total : (uint32_t)kMinLds;
+    if (smem > (uint32_t)(kMaxLds - 1024)) return hipErrorInvalidValue;
+    auto kern = decode_route_gateup_kernel<WDT>;
+    const hipError_t attr = allow_lds(kern);
+    if (attr != hipSuccess) return attr;
+    kern<<<cu_count(), kGuWaves * 64, smem, stream>>>(f);
     return hipGetLastError();
 }
 
@@ -264,14 +646,37 @@ bool decode_path(int act_dtype, int T, int H, int I, int E, int k) {
     return (int64_t)T * H * 2 < lim && rows * I * 2 < lim && (int64_t)H * I * 2 < lim;
 }
 
+// The fused routing + gate/up kernel serves decode problems with a small
+// batch and router (its LDS holds the logits, the selection and the order).
+bool decode_fused(int act_dtype, int T, int H, int I, int E, int k) {
+    if (!decode_path(act_dtype, T, H, I, E, k)) return false;
+    if (T < 1 || T > kFMaxT || E > kFMaxE) return false;
+    const int max_tiles = (T * k + kDecRows - 1) / kDecRows + E;
+    return flayout(T, k, max_tiles).total <= (uint32_t)(kMaxLds - 1024);
+}
+
+size_t decode_logit_part_bytes(int T, int E) { return (size_t)kLogitSlices * T * E * 4; }
+
+hipError_t launch_decode_logits(const void* h, const void* w_router, int T, int H, int E, float* part,
+                                hipStream_t stream) {
+    const dim3 grid(kLogitSlices, ((T + 15) / 16) * ((E + 15) / 16));
+    decode_logits_kernel<<<grid, 64, 0, stream>>>(reinterpret_cast<const uint16_t*>(h),
+                                                  reinterpret_cast<const uint16_t*>(w_router), T, E, H, part);
+    return hipGetLastError();
+}
+
 int decode_block_m() { return kDecRows; }
 
 hipError_t launch_gateup_decode(const GemmProblem& p, hipStream_t stream) {
-    return p.expert_dtype == DT_MXFP4 ? launch_dec<0, DT_MXFP4>(p, stream) : launch_dec<0, DT_BF16>(p, stream);
+    return p.expert_dtype == DT_MXFP4 ? launch_gu<DT_MXFP4>(p, stream) : launch_gu<DT_BF16>(p, stream);
+}
+
+hipError_t launch_route_gateup_decode(const GemmProblem& p, const FusedRouting& r, hipStream_t stream) {
+    return p.expert_dtype == DT_MXFP4 ? launch_fused<DT_MXFP4>(p, r, stream) : launch_fused<DT_BF16>(p, r, stream);
 }
 
 hipError_t launch_down_decode(const GemmProblem& p, hipStream_t stream) {
-    return p.expert_dtype == DT_MXFP4 ? launch_dec<1, DT_MXFP4>(p, stream) : launch_dec<1, DT_BF16>(p, stream);
+    return p.expert_dtype == DT_MXFP4 ? launch_dn<DT_MXFP4>(p, stream) : launch_dn<DT_BF16>(p, stream);
 }
 
 }  // namespace moe

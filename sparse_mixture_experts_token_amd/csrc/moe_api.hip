@@ -37,9 +37,11 @@ int check_problem(const moe_problem* p) {
 
 // Workspace regions, in order.
 struct Layout {
-    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, queues, work0, work1, act, y, total;
+    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, queues, work0, work1, part, act, y,
+        total;
     int nblk, max_tiles, BM, nc0, nc1;
     bool decode;
+    bool fused;  // routing computed inside the gate/up kernel (small decode problems)
     bool lists;  // prefill work lists are built
 };
 
@@ -47,6 +49,7 @@ Layout layout(const moe_problem* p) {
     Layout L{};
     const size_t tk = (size_t)p->T * p->k;
     L.decode = moe::decode_path(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
+    L.fused = moe::decode_fused(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
     L.BM = L.decode ? moe::decode_block_m() : moe::gemm_block_m(p->act_dtype, p->expert_dtype, p->T, p->k, p->E);
     L.nblk = (p->T + moe::kRouterTokens - 1) / moe::kRouterTokens;
     L.max_tiles = (int)((tk + L.BM - 1) / L.BM) + p->E;
@@ -68,6 +71,7 @@ Layout layout(const moe_problem* p) {
     L.nc1 = L.lists ? moe::bf16_col_tiles(p->H, 1) : 0;
     L.work0 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc0 * 4);
     L.work1 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc1 * 4);
+    L.part = o;     o = align_up(o + (L.fused ? moe::decode_logit_part_bytes(p->T, p->E) : 0));
     L.act = o;      o = align_up(o + tk * p->I * act_bytes(p->act_dtype));
     L.y = o;        o = align_up(o + tk * p->H * 4);
     L.total = o;
@@ -169,17 +173,23 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     };
 
     hipError_t e = hipSuccess;
-    mark(0);
-    e = moe::launch_router(p->act_dtype, h, w->w_router, w->b_router, p->T, p->H, p->E, p->k, logits, topk_idx,
-                           topk_w, blk, rank, stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    mark(1);
     moe::WorkList wl0{L.lists ? (int32_t*)(ws + L.work0) : nullptr, ntiles + 1, L.nc0};
     moe::WorkList wl1{L.lists ? (int32_t*)(ws + L.work1) : nullptr, ntiles + 2, L.nc1};
     int32_t* queues = (int32_t*)(ws + L.queues);
-    e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
-                               L.max_tiles, wl0, wl1, queues, moe::kNumQueues, stream);
+    float* part = (float*)(ws + L.part);
+    mark(0);
+    if (L.fused)
+        e = moe::launch_decode_logits(h, w->w_router, p->T, p->H, p->E, part, stream);
+    else
+        e = moe::launch_router(p->act_dtype, h, w->w_router, w->b_router, p->T, p->H, p->E, p->k, logits, topk_idx,
+                               topk_w, blk, rank, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(1);
+    if (!L.fused) {
+        e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
+                                   L.max_tiles, wl0, wl1, queues, moe::kNumQueues, stream);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
     mark(2);
 
     moe::GemmProblem g{};
@@ -202,7 +212,12 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     g.y = y;
     g.decode = L.decode;
     g.queues = queues;
-    e = moe::launch_gateup(g, stream);
+    if (L.fused) {
+        const moe::FusedRouting fr{part, w->b_router, logits, topk_idx, topk_w, offsets, perm, inv, tiles, ntiles};
+        e = moe::launch_route_gateup_decode(g, fr, stream);
+    } else {
+        e = moe::launch_gateup(g, stream);
+    }
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(3);
     e = moe::launch_down(g, stream);

@@ -202,6 +202,28 @@ bool decode_path(int act_dtype, int T, int H, int I, int E, int k);
 int decode_block_m();
 hipError_t launch_gateup_decode(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down_decode(const GemmProblem& p, hipStream_t stream);
+// Small decode problems (decode_fused true) run stages 0-2 as two kernels:
+// partial router logits (launch_decode_logits), then one kernel in which
+// every workgroup completes the routing of the batch, workgroup 0 writes it
+// to these buffers (the same contents the router and the route scan
+// produce), and the gate/up product follows.
+struct FusedRouting {
+    const float* part;  // partial logits, decode_logit_part_bytes()
+    const void* b_router;
+    float* logits;  // optional
+    int32_t* topk_idx;
+    float* topk_w;
+    int32_t* offsets;
+    int32_t* perm_src;
+    int32_t* inv;
+    Tile* tiles;
+    int32_t* n_tiles;
+};
+bool decode_fused(int act_dtype, int T, int H, int I, int E, int k);
+size_t decode_logit_part_bytes(int T, int E);
+hipError_t launch_decode_logits(const void* h, const void* w_router, int T, int H, int E, float* part,
+                                hipStream_t stream);
+hipError_t launch_route_gateup_decode(const GemmProblem& p, const FusedRouting& r, hipStream_t stream);
 int mxfp4_max_k();                   // largest H or I the MXFP4 kernels take
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, hipStream_t stream);

@@ -69,6 +69,9 @@ EDGE = [
     synth.Config(111, "decode-mxfp4-K-tails", T=20, H=192, I=320, E=6, k=3, act="bf16", expert="mxfp4"),
     synth.Config(112, "decode-several-tiles-per-expert", T=64, H=128, I=128, E=8, k=2, act="bf16", expert="bf16"),
     synth.Config(113, "decode-one-token", T=1, H=256, I=192, E=16, k=4, act="bf16", expert="mxfp4"),
+    # routing computed inside the gate/up kernel (T <= 64, E <= 64): its largest shape and one expert
+    synth.Config(114, "decode-fused-64-tokens-64-experts", T=64, H=256, I=128, E=64, k=16, act="bf16", expert="bf16"),
+    synth.Config(115, "decode-fused-single-expert", T=16, H=64, I=64, E=1, k=1, act="bf16", expert="bf16"),
 ]
 
 
