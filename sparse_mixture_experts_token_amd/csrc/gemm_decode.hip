@@ -31,11 +31,12 @@
 // which would leave only a few loads in flight); the down product also keeps
 // the next step's loads in flight while multiplying.
 //
-// Work split.  Gate/up runs with one workgroup per CU: the (tile, weight row)
-// pairs are split into equal contiguous ranges, one per workgroup, and each
-// range into equal sub-ranges, one per wave, with boundaries on multiples of
-// four rows; a wave walks its sub-range in passes of at most 32 rows.  Down
-// (half the bytes) runs one 32-row block per wave.
+// Work split.  bf16 gate/up runs with one workgroup per CU: the (tile, weight
+// row) pairs are split into equal contiguous ranges, one per workgroup, and
+// each range into equal sub-ranges, one per wave, with boundaries on
+// multiples of four rows; a wave walks its sub-range in passes of at most 32
+// rows.  Down, and MXFP4 gate/up, run one 32-row block per wave with the next
+// K step's loads in flight (measured faster for these).
 //
 // Fused routing.  When the batch and the router are small (T <= 64, E <= 64)
 // a small kernel writes partial router logits (K split into slices), and
@@ -290,25 +291,25 @@ __device__ __forceinline__ void balanced_share(const DArgs& a, const Tile* tiles
     }
 }
 
-// Gate/up over the tile list written by the route scan.
-template <int WDT>
-__global__ __launch_bounds__(kGuWaves * 64) void decode_gateup_kernel(DArgs a) {
+// Balanced ranges over the tile list written by the route scan.
+template <int MODE, int WDT, int DEPTH>
+__global__ __launch_bounds__(kGuWaves * 64) void decode_balanced_kernel(DArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int ntl = min(a.n_tiles[0], a.max_tiles);
-    balanced_share<0, WDT, 1, kGuWaves>(a, a.tiles, a.perm_src, ntl, wave, lane);
+    balanced_share<MODE, WDT, DEPTH, kGuWaves>(a, a.tiles, a.perm_src, ntl, wave, lane);
 }
 
-// Down: wave q takes 32-row block q % (N/32) of tile q / (N/32).
-template <int WDT>
-__global__ __launch_bounds__(kDnWaves * 64) void decode_down_kernel(DArgs a) {
+// One 32-row block per wave: wave q takes block q % (N/32) of tile q / (N/32).
+template <int MODE, int WDT, int DEPTH>
+__global__ __launch_bounds__(kDnWaves * 64) void decode_block_kernel(DArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int ntl = min(a.n_tiles[0], a.max_tiles);
     const int ncb = a.N / kDecCols;
     const int q = blockIdx.x * kDnWaves + wave;
     const int mt = q / ncb, cb = q - mt * ncb;
     if (mt >= ntl) return;  // wave-uniform; this kernel has no barriers
-    decode_pass<1, WDT, 2>(a, a.tiles[mt], a.perm_src, (uint32_t)(cb * kDecCols), (uint32_t)((cb + 1) * kDecCols),
-                           lane);
+    decode_pass<MODE, WDT, DEPTH>(a, a.tiles[mt], a.perm_src, (uint32_t)(cb * kDecCols),
+                                  (uint32_t)((cb + 1) * kDecCols), lane);
 }
 
 // ------------------------------------------------ fused routing + gate/up --
@@ -537,7 +538,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
     __syncthreads();
 
     // 4. gate/up: this workgroup's share of the tiles
-    balanced_share<0, WDT, 1, kGuWaves>(a, tl, perm, min(toff[E], a.max_tiles), wave, lane);
+    balanced_share<0, WDT, WDT == DT_MXFP4 ? 2 : 1, kGuWaves>(a, tl, perm, min(toff[E], a.max_tiles), wave, lane);
 }
 
 DArgs make_dargs(const GemmProblem& p, int mode) {
@@ -590,22 +591,34 @@ hipError_t allow_lds(Kern kern) {
     return attr;
 }
 
+template <int MODE, int WDT, int DEPTH>
+hipError_t launch_blocks(const GemmProblem& p, hipStream_t stream) {
+    const DArgs a = make_dargs(p, MODE);
+    const int blocks = (int)(((size_t)p.max_tiles * (a.N / kDecCols) + kDnWaves - 1) / kDnWaves);
+    decode_block_kernel<MODE, WDT, DEPTH><<<blocks, kDnWaves * 64, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+// bf16 gate/up: balanced ranges, one K step in flight.  MXFP4 gate/up moves
+// a quarter of the bytes per K step, so it keeps two steps in flight and one
+// block per wave (many more waves in flight than one workgroup per CU holds).
 template <int WDT>
 hipError_t launch_gu(const GemmProblem& p, hipStream_t stream) {
-    const DArgs a = make_dargs(p, 0);
-    auto kern = decode_gateup_kernel<WDT>;
-    const hipError_t attr = allow_lds(kern);
-    if (attr != hipSuccess) return attr;
-    kern<<<cu_count(), kGuWaves * 64, kMinLds, stream>>>(a);
-    return hipGetLastError();
+    if constexpr (WDT == DT_MXFP4) {
+        return launch_blocks<0, WDT, 2>(p, stream);
+    } else {
+        const DArgs a = make_dargs(p, 0);
+        auto kern = decode_balanced_kernel<0, WDT, 1>;
+        const hipError_t attr = allow_lds(kern);
+        if (attr != hipSuccess) return attr;
+        kern<<<cu_count(), kGuWaves * 64, kMinLds, stream>>>(a);
+        return hipGetLastError();
+    }
 }
 
 template <int WDT>
 hipError_t launch_dn(const GemmProblem& p, hipStream_t stream) {
-    const DArgs a = make_dargs(p, 1);
-    const int blocks = (int)(((size_t)p.max_tiles * (a.N / kDecCols) + kDnWaves - 1) / kDnWaves);
-    decode_down_kernel<WDT><<<blocks, kDnWaves * 64, 0, stream>>>(a);
-    return hipGetLastError();
+    return launch_blocks<1, WDT, 2>(p, stream);
 }
 
 template <int WDT>
