@@ -6,13 +6,13 @@
 //   gate/up:  act[r, :] = silu(x_r W_gate[e]^T) * (x_r W_up[e]^T),  x_r = h[token of row r]
 //   down:     y[a, :]   = p_a * (act[r, :] W_down[e]^T),            a = perm_src[r]
 //
-// Workgroup tile: BM = 256 rows of one expert x BN = 128 weight rows per
-// matrix (gate/up: 128 of gate and the same 128 of up; down: 128 of W_down),
-// eight waves in a 4 x 2 layout, two per SIMD, so that one wave's MFMAs cover
-// the other's LDS and DMA issue.  Wave (wm, wn) owns the 32-row groups wm and
+// Workgroup tile: BM = 256 rows of one expert x BN weight rows per matrix
+// (gate/up: 128 of gate and the same 128 of up; down: 256 of W_down), eight
+// waves in a 4 x 2 layout, two per SIMD, so that one wave's MFMAs cover the
+// other's LDS and DMA issue.  Wave (wm, wn) owns the 32-row groups wm and
 // wm + 4 and half of the tile's weight rows of every matrix, as 32x32x16 bf16
 // MFMA tiles with fp32 accumulators (gate/up: 2 x 2 of gate and 2 x 2 of up,
-// so SiLU*up is formed in registers; down: 2 x 2).
+// so SiLU*up is formed in registers; down: 2 x 4).
 //
 // Operands reach LDS by buffer-to-LDS DMA.  What limits such a kernel on this
 // hardware is how many cache lines one load instruction touches: 64 lanes x
@@ -26,8 +26,8 @@
 // 16q + 8(l/32) .. +7 of step q) spreads every group of 16 lanes over all
 // LDS banks.
 //
-// Software pipeline: an LDS ring of two 64 KB stages (gate/up) or three 48 KB
-// stages (down).  Within a stage the fragments of K steps 2,3 are read while
+// Software pipeline: an LDS ring of two 64 KB stages (three smaller ones for
+// MXFP4 weights).  Within a stage the fragments of K steps 2,3 are read while
 // steps 0,1 compute; then, behind the one barrier per stage, the slot just
 // released is refilled by DMA and steps 0,1 of the next stage are read while
 // steps 2,3 compute.  sched_group_barrier spreads the DMA and LDS reads
@@ -43,11 +43,12 @@
 // scale, decoded exactly to bf16 right before its MFMA (hardware scaled
 // conversion for scales 2..252, integer path for the extremes).
 //
-// Block order: each XCD (blocks are dealt round-robin to 8) takes a
-// contiguous range of a work list built with the routing tables: experts in
-// order, for each expert its column tiles, for each column tile all the
-// expert's row tiles, so the row tiles sharing a weight tile run together on
-// one XCD and its L2 serves the repeats.
+// Block order: persistent workgroups, one per CU.  Each XCD (blocks are dealt
+// round-robin to 8) drains a contiguous range of a work list built with the
+// routing tables - experts in order, for each expert its column tiles, for
+// each column tile all the expert's row tiles - through its own work-queue
+// counter, so the row tiles sharing a weight tile run together on one XCD
+// and its L2 serves the repeats.
 #include "moe_internal.h"
 
 namespace moe {
