@@ -336,7 +336,6 @@ __global__ __launch_bounds__(kDnWaves * 64) void decode_block_kernel(DArgs a) {
 
 constexpr int kFMaxT = 64;        // tokens (one bit each in a 64-bit mask)
 constexpr int kFMaxE = 64;        // experts (one per lane in top-k)
-constexpr int kLogitSlices = 8;   // K slices of the partial logits
 constexpr int kLogitSteps = 12;   // 32-wide K steps per batch of loads in the logits kernel
 
 // Partial logits: block (ks, tile) computes token tile tile / ET x expert
@@ -407,14 +406,6 @@ __host__ __device__ inline FLayout flayout(int T, int k, int max_tiles) {
     L.tiles = o; o += align16((uint32_t)max_tiles * sizeof(Tile));
     L.total = o;
     return L;
-}
-
-// Larger value first (NaN last, -0 as +0), then the lower expert index.
-__device__ __forceinline__ unsigned long long order_key(float v, int e) {
-    uint32_t u = __float_as_uint(v);
-    if (u == 0x80000000u) u = 0u;
-    u = (v != v) ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
-    return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
 }
 
 template <int WDT>

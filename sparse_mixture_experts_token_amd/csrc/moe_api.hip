@@ -42,6 +42,7 @@ struct Layout {
     int nblk, max_tiles, BM, nc0, nc1;
     bool decode;
     bool fused;  // routing computed inside the gate/up kernel (small decode problems)
+    bool plogits;  // router logits from the partial-logits kernel (small bf16 batches)
     bool lists;  // prefill work lists are built
 };
 
@@ -50,6 +51,7 @@ Layout layout(const moe_problem* p) {
     const size_t tk = (size_t)p->T * p->k;
     L.decode = moe::decode_path(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
     L.fused = moe::decode_fused(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
+    L.plogits = p->act_dtype == MOE_BF16 && p->T <= 64;
     L.BM = L.decode ? moe::decode_block_m() : moe::gemm_block_m(p->act_dtype, p->expert_dtype, p->T, p->k, p->E);
     L.nblk = (p->T + moe::kRouterTokens - 1) / moe::kRouterTokens;
     L.max_tiles = (int)((tk + L.BM - 1) / L.BM) + p->E;
@@ -71,7 +73,7 @@ Layout layout(const moe_problem* p) {
     L.nc1 = L.lists ? moe::bf16_col_tiles(p->H, 1) : 0;
     L.work0 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc0 * 4);
     L.work1 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc1 * 4);
-    L.part = o;     o = align_up(o + (L.fused ? moe::decode_logit_part_bytes(p->T, p->E) : 0));
+    L.part = o;     o = align_up(o + (L.plogits ? moe::decode_logit_part_bytes(p->T, p->E) : 0));
     L.act = o;      o = align_up(o + tk * p->I * act_bytes(p->act_dtype));
     L.y = o;        o = align_up(o + tk * p->H * 4);
     L.total = o;
@@ -178,12 +180,15 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     int32_t* queues = (int32_t*)(ws + L.queues);
     float* part = (float*)(ws + L.part);
     mark(0);
-    if (L.fused)
+    if (L.plogits) {
         e = moe::launch_decode_logits(h, w->w_router, p->T, p->H, p->E, part, stream);
-    else
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (!L.fused) {
         e = moe::launch_router(p->act_dtype, h, w->w_router, w->b_router, p->T, p->H, p->E, p->k, logits, topk_idx,
-                               topk_w, blk, rank, stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
+                               topk_w, blk, rank, L.plogits ? part : nullptr, stream);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
     mark(1);
     if (!L.fused) {
         e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,

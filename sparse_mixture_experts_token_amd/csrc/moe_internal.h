@@ -22,6 +22,9 @@ enum : int { DT_F32 = 0, DT_BF16 = 1, DT_MXFP4 = 2 };
 
 // Router/top-k tile: tokens per workgroup.
 constexpr int kRouterTokens = 16;
+// Small batches (T <= 64, bf16): the router logits are first written as
+// partial sums over this many interleaved K slices by launch_decode_logits.
+constexpr int kLogitSlices = 8;
 
 // One row-tile of one expert in the expert-major order (built on the device).
 struct Tile {
@@ -118,6 +121,18 @@ __device__ __forceinline__ void decode_mxfp4_32(const u32x4& q, uint32_t scale, 
     }
 }
 
+// -------------------------------------------------------------- top-k order --
+// 64-bit key of logit v of expert e: the value mapped to an order-preserving
+// unsigned integer (NaN lowest, -0 as +0) above the complement of the index,
+// so "key a > key b" is "a has the larger value, or the same value and the
+// lower index" - the selection order of the top-k (ties to the lower index).
+__device__ __forceinline__ unsigned long long order_key(float v, int e) {
+    uint32_t u = __float_as_uint(v);
+    if (u == 0x80000000u) u = 0u;
+    u = (v != v) ? 0u : ((u & 0x80000000u) ? ~u : (u | 0x80000000u));
+    return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
+}
+
 // ------------------------------------------------------------- MFMA wrappers --
 // 32x32x16 bf16: lane l holds A[l%32][8(l/32)+0..7], B[8(l/32)+0..7][l%32];
 // D[4i+j] is row 8i+4(l/32)+j, column l%32.
@@ -142,10 +157,12 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 // All launchers enqueue on `stream` and return hipGetLastError().
 
 // Stage 0: router logits + top-k + selected softmax + per-tile counts/ranks.
+// With part non-null the logits are the slice sums of part [kLogitSlices][T][E]
+// (launch_decode_logits) plus the bias, instead of being computed from h.
 hipError_t launch_router(int act_dtype, const void* h, const void* w_router, const void* b_router,
                          int T, int H, int E, int k, float* logits_opt, int32_t* topk_idx,
                          float* topk_w, int32_t* blk_counts /*[E][nblk]*/, int32_t* local_rank,
-                         hipStream_t stream);
+                         const float* part, hipStream_t stream);
 
 // Stage 1: scan + stable permutation + tile list + GEMM work lists.
 // A work list enumerates (row tile, column tile) pairs as

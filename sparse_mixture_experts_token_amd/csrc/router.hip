@@ -35,10 +35,12 @@ struct RouterSmem {
     static __host__ __device__ size_t part_bytes() { return (size_t)NW * BT * kCBMax * 16 * 4; }
     // selection positions [BT][Ep] u16 reuse the partial-sum region once the logits are done
     static __host__ __device__ size_t selpos_off(int Ep) { return part_off(Ep); }
-    static __host__ __device__ size_t bytes(int Ep) {
+    // the bias [Ep] f32
+    static __host__ __device__ size_t bias_off(int Ep) {
         const size_t sel = (size_t)BT * Ep * 2;
         return part_off(Ep) + (sel > part_bytes() ? sel : part_bytes());
     }
+    static __host__ __device__ size_t bytes(int Ep) { return bias_off(Ep) + (size_t)Ep * 4; }
 };
 
 template <typename TA>
@@ -171,12 +173,13 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
                                                      const TA* __restrict__ br, int T, int H, int E, int k,
                                                      float* __restrict__ logits_opt, int32_t* __restrict__ topk_idx,
                                                      float* __restrict__ topk_w, int32_t* __restrict__ blk_counts,
-                                                     int32_t* __restrict__ local_rank) {
+                                                     int32_t* __restrict__ local_rank, const float* __restrict__ lpart) {
     extern __shared__ __align__(16) unsigned char smem[];
     const int Ep = (E + 63) & ~63;  // padded so every lane owns Ep/64 columns
     float* s_lds = reinterpret_cast<float*>(smem + RouterSmem::logits_off());
     float* part = reinterpret_cast<float*>(smem + RouterSmem::part_off(Ep));
     uint16_t* selpos = reinterpret_cast<uint16_t*>(smem + RouterSmem::selpos_off(Ep));
+    float* s_bias = reinterpret_cast<float*>(smem + RouterSmem::bias_off(Ep));
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -184,11 +187,32 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
     const int t0 = blockIdx.x * BT;
     const int nblk = gridDim.x;
 
+    // the bias is read once, ahead of the logits loads, and parked in LDS with
+    // the first partial sums (its latency hides behind theirs); the bf16
+    // variant for 33..64 experts has no register to spare for it and reads it
+    // in the reduction instead
+    constexpr bool kBiasEarly = !(sizeof(TA) == 2 && CB == 4 && NV == 1);
+    const float bias_r = (kBiasEarly && br && tid < E) ? load_scalar(br, tid) : 0.f;
+
     // ---------------------------------------------------------- logits --
     const int arow = min(t0 + (lane & 15), T - 1);
     const TA* hrow = h + (size_t)arow * H;
     const int ncb = (E + 15) >> 4;
 
+    if (lpart) {
+        // the slice sums written by the small-batch logits kernel, in slice order, then the bias
+        for (int i = tid; i < BT * E; i += kThreads) {
+            const int row = i / E, e = i - row * E, t = t0 + row;
+            if (t < T) {
+                float v = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < kLogitSlices; ++ks) v += lpart[((size_t)ks * T + t) * E + e];
+                if (br) v += load_scalar(br, e);
+                s_lds[row * Ep + e] = v;
+            }
+        }
+        __syncthreads();
+    } else
     for (int cb0 = 0; cb0 < ncb; cb0 += CB) {
         f32x4 acc[CB];
         logits_pass<TA, CB>(hrow, wr, H, E, cb0, wave, lane, acc);
@@ -200,6 +224,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
                 int row = (lane >> 4) * 4 + j;
                 part[((wave * BT) + row) * (kCBMax * 16) + c * 16 + (lane & 15)] = acc[c][j];
             }
+        if (kBiasEarly && cb0 == 0 && tid < E) s_bias[tid] = bias_r;
         __syncthreads();
         // fixed-order reduction over the waves, then the bias
         for (int i = tid; i < BT * CB * 16; i += kThreads) {
@@ -210,7 +235,10 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
                 float v = part[row * (kCBMax * 16) + col];
 #pragma unroll
                 for (int w = 1; w < NW; ++w) v += part[(w * BT + row) * (kCBMax * 16) + col];
-                if (br) v += load_scalar(br, e);
+                if constexpr (kBiasEarly)
+                    v += s_bias[e];
+                else if (br)
+                    v += load_scalar(br, e);
                 s_lds[row * Ep + e] = v;
             }
         }
@@ -220,6 +248,45 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
     __syncthreads();
 
     // -------------------------------------------- top-k + selected softmax --
+    if constexpr (NV == 1) {
+        // one expert per lane: selection by rank.  Expert e is chosen when
+        // fewer than k experts have a larger order key (value, then lower
+        // index); positions are in ascending expert order.
+        for (int tt = wave; tt < BT; tt += NW) {
+            const int t = t0 + tt;
+            if (t >= T) break;  // wave-uniform
+            const bool ok = lane < E;
+            const float v = ok ? s_lds[tt * Ep + lane] : 0.f;
+            const unsigned long long mine = ok ? order_key(v, lane) : 0ull;
+            const f32x4* row = reinterpret_cast<const f32x4*>(s_lds + tt * Ep);
+            int rank = 0;
+            for (int c0 = 0; c0 < 16; c0 += 4) {  // four 16-byte reads at a time
+#pragma unroll
+                for (int c = c0; c < c0 + 4; ++c) {
+                    const f32x4 q = row[c];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int e2 = 4 * c + j;
+                        rank += ((e2 < E) & (order_key(q[j], e2) > mine)) ? 1 : 0;
+                    }
+                }
+            }
+            if (logits_opt && ok) logits_opt[(size_t)t * E + lane] = v;
+            const bool chosen = ok & (rank < k);
+            const uint64_t top = __ballot(ok & (rank == 0));
+            const float smax = lane_f(v, (int)__builtin_ctzll(top));
+            const float z = chosen ? expf(v - smax) : 0.f;
+            const float denom = wave_sum(z);
+            const uint64_t bal = __ballot(chosen);
+            const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            const int pos = __popcll(bal & lt);
+            if (chosen) {
+                topk_idx[(size_t)t * k + pos] = lane;
+                topk_w[(size_t)t * k + pos] = z / denom;
+                selpos[tt * Ep + lane] = (uint16_t)(pos + 1);
+            }
+        }
+    } else
     // Lane owns experts e = lane + 64 i, i < NV (NV = padded E / 64).
     for (int tt = wave; tt < BT; tt += NW) {
         const int t = t0 + tt;
@@ -297,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
 template <typename TA, int CB, int NV>
 hipError_t launch_k(const void* h, const void* w_router, const void* b_router, int T, int H, int E, int k,
                     float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, int32_t* local_rank,
-                    hipStream_t stream) {
+                    const float* part, hipStream_t stream) {
     const int nblk = (T + BT - 1) / BT;
     const size_t smem = RouterSmem::bytes((E + 63) & ~63);
     auto kern = router_kernel<TA, CB, NV>;
@@ -305,7 +372,7 @@ hipError_t launch_k(const void* h, const void* w_router, const void* b_router, i
         hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)RouterSmem::bytes(1024));
     if (attr != hipSuccess) return attr;
     kern<<<nblk, kThreads, smem, stream>>>((const TA*)h, (const TA*)w_router, (const TA*)b_router, T, H, E, k, logits_opt,
-                                      topk_idx, topk_w, blk_counts, local_rank);
+                                      topk_idx, topk_w, blk_counts, local_rank, part);
     return hipGetLastError();
 }
 
@@ -313,10 +380,10 @@ hipError_t launch_k(const void* h, const void* w_router, const void* b_router, i
 template <typename TA>
 hipError_t launch_t(const void* h, const void* w_router, const void* b_router, int T, int H, int E, int k,
                     float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* blk_counts, int32_t* local_rank,
-                    hipStream_t stream) {
+                    const float* part, hipStream_t stream) {
 #define MOE_ROUTER_LAUNCH(CB, NV)                                                                                  \
     return launch_k<TA, CB, NV>(h, w_router, b_router, T, H, E, k, logits_opt, topk_idx, topk_w, blk_counts, \
-                                local_rank, stream)
+                                local_rank, part, stream)
     if (E <= 16) MOE_ROUTER_LAUNCH(1, 1);
     if (E <= 32) MOE_ROUTER_LAUNCH(2, 1);
     if (E <= 64) MOE_ROUTER_LAUNCH(4, 1);
@@ -330,12 +397,12 @@ hipError_t launch_t(const void* h, const void* w_router, const void* b_router, i
 
 hipError_t launch_router(int act_dtype, const void* h, const void* w_router, const void* b_router, int T, int H,
                          int E, int k, float* logits_opt, int32_t* topk_idx, float* topk_w, int32_t* blk_counts,
-                         int32_t* local_rank, hipStream_t stream) {
+                         int32_t* local_rank, const float* part, hipStream_t stream) {
     if (act_dtype == DT_BF16)
         return launch_t<uint16_t>(h, w_router, b_router, T, H, E, k, logits_opt, topk_idx, topk_w, blk_counts,
-                                  local_rank, stream);
+                                  local_rank, part, stream);
     return launch_t<float>(h, w_router, b_router, T, H, E, k, logits_opt, topk_idx, topk_w, blk_counts, local_rank,
-                           stream);
+                           part, stream);
 }
 
 size_t router_smem_bytes(int E) { return RouterSmem::bytes((E + 63) & ~63); }
