@@ -35,8 +35,9 @@
 // row) pairs are split into equal contiguous ranges, one per workgroup, and
 // each range into equal sub-ranges, one per wave, with boundaries on
 // multiples of four rows; a wave walks its sub-range in passes of at most 32
-// rows.  Down, and MXFP4 gate/up, run one 32-row block per wave with the next
-// K step's loads in flight (measured faster for these).
+// rows.  Down (64-row blocks) and MXFP4 gate/up (32-row blocks) run one block
+// per wave, in one-wave workgroups, with the next K step's loads in flight
+// (measured faster for these).
 //
 // Fused routing.  When the batch and the router are small (T <= 64, E <= 64)
 // a small kernel writes partial router logits (K split into slices), and
@@ -55,7 +56,7 @@ constexpr int kPanels = 2;             // 16-row weight panels per pass
 constexpr int kDecCols = 16 * kPanels; // weight rows per pass
 constexpr int kRowAlign = 4;           // range boundaries: whole 8-/16-byte output stores
 constexpr int kGuWaves = 12;           // gate/up: waves per workgroup, one workgroup per CU
-constexpr int kDnWaves = 4;            // down: waves per workgroup, one 32-row block per wave
+constexpr int kBlkWaves = 1;           // one-block-per-wave kernels: waves per workgroup (independent)
 constexpr int kMinLds = 96 * 1024;     // LDS per gate/up workgroup: room for no second one on the CU
 constexpr uint32_t kOob = 0x7ffffff0u; // byte offset past every buffer used here (all < 2^30 bytes)
 
@@ -90,22 +91,22 @@ __device__ __forceinline__ void load_b(buf_rsrc b, uint32_t b_base, bool has_row
 // The loads of one 128-wide K step, in flat register arrays (weights of
 // panel p: wq[4p..4p+3] for bf16, wq[p] + ws[p] for MXFP4; up weights in
 // uq / us; activations in b).
-template <int MODE, int WDT>
+template <int MODE, int WDT, int NP>
 struct Batch {
-    static constexpr int NQ = WDT == DT_MXFP4 ? kPanels : 4 * kPanels;
+    static constexpr int NQ = WDT == DT_MXFP4 ? NP : 4 * NP;
     u32x4 wq[NQ];
     u32x4 uq[MODE == 0 ? NQ : 1];
-    uint32_t ws[kPanels];
-    uint32_t us[kPanels];
+    uint32_t ws[NP];
+    uint32_t us[NP];
     u32x4 b[4];
 };
 
-template <int MODE, int WDT>
-__device__ __forceinline__ void issue(Batch<MODE, WDT>& x, buf_rsrc w0, buf_rsrc w1, buf_rsrc s0, buf_rsrc s1,
-                                      buf_rsrc bsrc, const uint32_t (&n)[kPanels], const bool (&nv)[kPanels],
+template <int MODE, int WDT, int NP>
+__device__ __forceinline__ void issue(Batch<MODE, WDT, NP>& x, buf_rsrc w0, buf_rsrc w1, buf_rsrc s0, buf_rsrc s1,
+                                      buf_rsrc bsrc, const uint32_t (&n)[NP], const bool (&nv)[NP],
                                       uint32_t b_base, bool has_row, uint32_t K, uint32_t g, uint32_t qd) {
 #pragma unroll
-    for (int p = 0; p < kPanels; ++p) {
+    for (int p = 0; p < NP; ++p) {
         if constexpr (WDT == DT_MXFP4) {
             const uint32_t kq = g * 128 + qd * 32;
             const bool kv = nv[p] && kq < K;
@@ -138,13 +139,13 @@ __device__ __forceinline__ void frags(const u32x4 (&q)[NQ], uint32_t scale, int 
         f[j] = __builtin_bit_cast(bf16x8, u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
 }
 
-template <int MODE, int WDT>
-__device__ __forceinline__ void compute(const Batch<MODE, WDT>& x, f32x4 (&acc0)[kPanels], f32x4 (&acc1)[kPanels]) {
+template <int MODE, int WDT, int NP>
+__device__ __forceinline__ void compute(const Batch<MODE, WDT, NP>& x, f32x4 (&acc0)[NP], f32x4 (&acc1)[NP]) {
     if constexpr (WDT != DT_MXFP4) {
         // each 16-byte register straight into its MFMA (no fragment copies,
         // which would keep the batch in scratch memory)
 #pragma unroll
-        for (int p = 0; p < kPanels; ++p)
+        for (int p = 0; p < NP; ++p)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bf16x8 bj = __builtin_bit_cast(bf16x8, x.b[j]);
@@ -153,7 +154,7 @@ __device__ __forceinline__ void compute(const Batch<MODE, WDT>& x, f32x4 (&acc0)
             }
     } else {
 #pragma unroll
-        for (int p = 0; p < kPanels; ++p) {
+        for (int p = 0; p < NP; ++p) {
             bf16x8 fa[4];
             frags<WDT>(x.wq, x.ws[p], p, fa);
 #pragma unroll
@@ -168,11 +169,11 @@ __device__ __forceinline__ void compute(const Batch<MODE, WDT>& x, f32x4 (&acc0)
     }
 }
 
-// One block: weight rows [c0, c1) (c1 - c0 <= 32, both multiples of four) of
-// the expert of `tile` against the tile's activation rows; perm holds the
+// One block: weight rows [c0, c1) (c1 - c0 <= 16 NP, both multiples of four)
+// of the expert of `tile` against the tile's activation rows; perm holds the
 // assignment of every expert-major row (global memory or LDS).  DEPTH = K
 // steps of loads in flight (1 or 2).
-template <int MODE, int WDT, int DEPTH>
+template <int MODE, int WDT, int DEPTH, int NP = kPanels>
 __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, const int32_t* perm, uint32_t c0,
                                             uint32_t c1, int lane) {
     const int e = tile.expert, row0 = tile.row_start, rows = tile.rows;
@@ -190,10 +191,10 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
     const buf_rsrc bsrc = make_rsrc(a.a_src, a.a_bytes);
 
     // weight operand: rows n[p] of expert e, present while below c1
-    uint32_t n[kPanels];
-    bool nv[kPanels];
+    uint32_t n[NP];
+    bool nv[NP];
 #pragma unroll
-    for (int p = 0; p < kPanels; ++p) {
+    for (int p = 0; p < NP; ++p) {
         n[p] = c0 + (uint32_t)(p * 16 + r);
         nv[p] = n[p] < c1;
     }
@@ -211,29 +212,29 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
         s0 = s1 = w0;
     }
 
-    f32x4 acc0[kPanels], acc1[kPanels];
+    f32x4 acc0[NP], acc1[NP];
 #pragma unroll
-    for (int p = 0; p < kPanels; ++p) acc0[p] = acc1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < NP; ++p) acc0[p] = acc1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
     // Steps past the end read beyond K: zeros, no memory traffic.
     const uint32_t ng = (K + 127) / 128;
-    Batch<MODE, WDT> x0, x1;
+    Batch<MODE, WDT, NP> x0, x1;
     if constexpr (DEPTH == 1) {
         for (uint32_t g = 0; g < ng; ++g) {
-            issue<MODE, WDT>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g, qd);
+            issue<MODE, WDT, NP>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g, qd);
             __builtin_amdgcn_sched_barrier(0);
-            compute<MODE, WDT>(x0, acc0, acc1);
+            compute<MODE, WDT, NP>(x0, acc0, acc1);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else {
-        issue<MODE, WDT>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, 0, qd);
+        issue<MODE, WDT, NP>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, 0, qd);
         for (uint32_t g = 0; g < ng; g += 2) {
-            issue<MODE, WDT>(x1, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 1, qd);
+            issue<MODE, WDT, NP>(x1, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 1, qd);
             __builtin_amdgcn_sched_barrier(0);
-            compute<MODE, WDT>(x0, acc0, acc1);
+            compute<MODE, WDT, NP>(x0, acc0, acc1);
             __builtin_amdgcn_sched_barrier(0);
-            issue<MODE, WDT>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 2, qd);
+            issue<MODE, WDT, NP>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 2, qd);
             __builtin_amdgcn_sched_barrier(0);
-            compute<MODE, WDT>(x1, acc0, acc1);
+            compute<MODE, WDT, NP>(x1, acc0, acc1);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -245,7 +246,7 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
     if constexpr (MODE == 0) {
         uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (size_t)(row0 + r) * N;
 #pragma unroll
-        for (int p = 0; p < kPanels; ++p) {
+        for (int p = 0; p < NP; ++p) {
             const uint32_t n0 = c0 + (uint32_t)(p * 16) + 4 * qd;
             if (n0 >= c1) continue;
             uint32_t v[4];
@@ -258,7 +259,7 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
         const float pw = a.topk_w[asg];
         float* orow = reinterpret_cast<float*>(a.out) + (size_t)asg * N;
 #pragma unroll
-        for (int p = 0; p < kPanels; ++p) {
+        for (int p = 0; p < NP; ++p) {
             const uint32_t n0 = c0 + (uint32_t)(p * 16) + 4 * qd;
             if (n0 >= c1) continue;
             *reinterpret_cast<float4*>(orow + n0) =
@@ -299,17 +300,19 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_balanced_kernel(DArgs a)
     balanced_share<MODE, WDT, DEPTH, kGuWaves>(a, a.tiles, a.perm_src, ntl, wave, lane);
 }
 
-// One 32-row block per wave: wave q takes block q % (N/32) of tile q / (N/32).
-template <int MODE, int WDT, int DEPTH>
-__global__ __launch_bounds__(kDnWaves * 64) void decode_block_kernel(DArgs a) {
+// One block of 16 NP weight rows per wave: wave q takes block q % nb of tile
+// q / nb, nb = ceil(N / (16 NP)).
+template <int MODE, int WDT, int DEPTH, int NP>
+__global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int ntl = min(a.n_tiles[0], a.max_tiles);
-    const int ncb = a.N / kDecCols;
-    const int q = blockIdx.x * kDnWaves + wave;
+    constexpr uint32_t kRows = 16 * NP;
+    const int ncb = (int)(((uint32_t)a.N + kRows - 1) / kRows);
+    const int q = blockIdx.x * kBlkWaves + wave;
     const int mt = q / ncb, cb = q - mt * ncb;
     if (mt >= ntl) return;  // wave-uniform; this kernel has no barriers
-    decode_pass<MODE, WDT, DEPTH>(a, a.tiles[mt], a.perm_src, (uint32_t)(cb * kDecCols),
-                                  (uint32_t)((cb + 1) * kDecCols), lane);
+    const uint32_t c0 = (uint32_t)cb * kRows;
+    decode_pass<MODE, WDT, DEPTH, NP>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane);
 }
 
 // ------------------------------------------------ fused routing + gate/up --
@@ -582,13 +585,16 @@ hipError_t allow_lds(Kern kern) {
     return attr;
 }
 
-template <int MODE, int WDT, int DEPTH>
+template <int MODE, int WDT, int DEPTH, int NP>
 hipError_t launch_blocks(const GemmProblem& p, hipStream_t stream) {
     const DArgs a = make_dargs(p, MODE);
-    const int blocks = (int)(((size_t)p.max_tiles * (a.N / kDecCols) + kDnWaves - 1) / kDnWaves);
-    decode_block_kernel<MODE, WDT, DEPTH><<<blocks, kDnWaves * 64, 0, stream>>>(a);
+    const size_t ncb = ((size_t)a.N + 16 * NP - 1) / (16 * NP);
+    const int blocks = (int)(((size_t)p.max_tiles * ncb + kBlkWaves - 1) / kBlkWaves);
+    decode_block_kernel<MODE, WDT, DEPTH, NP><<<blocks, kBlkWaves * 64, 0, stream>>>(a);
     return hipGetLastError();
 }
+
+constexpr int kDnPanels = 4;  // down: 16-row weight panels per wave (a tile's activation loads shared by 64 rows)
 
 // bf16 gate/up: balanced ranges, one K step in flight.  MXFP4 gate/up moves
 // a quarter of the bytes per K step, so it keeps two steps in flight and one
@@ -596,7 +602,7 @@ hipError_t launch_blocks(const GemmProblem& p, hipStream_t stream) {
 template <int WDT>
 hipError_t launch_gu(const GemmProblem& p, hipStream_t stream) {
     if constexpr (WDT == DT_MXFP4) {
-        return launch_blocks<0, WDT, 2>(p, stream);
+        return launch_blocks<0, WDT, 2, kPanels>(p, stream);
     } else {
         const DArgs a = make_dargs(p, 0);
         auto kern = decode_balanced_kernel<0, WDT, 1>;
@@ -609,7 +615,7 @@ hipError_t launch_gu(const GemmProblem& p, hipStream_t stream) {
 
 template <int WDT>
 hipError_t launch_dn(const GemmProblem& p, hipStream_t stream) {
-    return launch_blocks<1, WDT, 2>(p, stream);
+    return launch_blocks<1, WDT, 2, kDnPanels>(p, stream);
 }
 
 template <int WDT>
