@@ -340,6 +340,7 @@ __global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
 constexpr int kFMaxT = 64;        // tokens (one bit each in a 64-bit mask)
 constexpr int kFMaxE = 64;        // experts (one per lane in top-k)
 constexpr int kLogitSteps = 12;   // 32-wide K steps per batch of loads in the logits kernel
+constexpr int kFLogitsPerThread = (kFMaxT * kFMaxE + kGuWaves * 64 - 1) / (kGuWaves * 64);
 
 // Partial logits: block (ks, tile) computes token tile tile / ET x expert
 // tile tile % ET over the K steps s = ks (mod kLogitSlices).
@@ -411,6 +412,24 @@ __host__ __device__ inline FLayout flayout(int T, int k, int max_tiles) {
     return L;
 }
 
+// Number of the 2 NC keys at krow that exceed `mine`.  All reads are issued
+// before the first compare (a data-dependent exit between them would make
+// every read wait out its own latency).
+template <int NC>
+__device__ __forceinline__ int rank_of(const u32x4* krow, unsigned long long mine) {
+    u32x4 q[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c] = krow[c];
+    int rank = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const unsigned long long k0 = ((unsigned long long)q[c].y << 32) | q[c].x;
+        const unsigned long long k1 = ((unsigned long long)q[c].w << 32) | q[c].z;
+        rank += (k0 > mine ? 1 : 0) + (k1 > mine ? 1 : 0);
+    }
+    return rank;
+}
+
 template <int WDT>
 __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArgs f) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -429,21 +448,36 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool writer = blockIdx.x == 0;
 
-    // 1. logits = slices added in slice order, then the bias; their order keys
+    // 1. logits = slices added in slice order, then the bias; their order keys.
+    //    A thread owns logits tid, tid + 768, ... (at most kFLogitsPerThread)
+    //    and issues all their loads before summing: one round trip to L2.
     if (tid < kFMaxE) emask[tid] = 0ull;
-    for (int i = tid; i < T * kFMaxE; i += kGuWaves * 64) {
-        const int t = i / kFMaxE, e = i - t * kFMaxE;
-        unsigned long long key = 0ull;  // past E: below every key
-        if (e < E) {
+    for (int i = tid; i < T * kFMaxE; i += kGuWaves * 64)
+        if (i % kFMaxE >= E) skey[i] = 0ull;  // past E: below every key
+    {
+        float pv[kFLogitsPerThread][kLogitSlices], bv[kFLogitsPerThread];
+#pragma unroll
+        for (int j = 0; j < kFLogitsPerThread; ++j) {
+            const int i = tid + j * kGuWaves * 64;
+            const bool in = i < T * E;
+            const int t = in ? i / E : 0, e = in ? i - t * E : 0;
+#pragma unroll
+            for (int ks = 0; ks < kLogitSlices; ++ks) pv[j][ks] = in ? f.part[((size_t)ks * T + t) * E + e] : 0.f;
+            bv[j] = (in && f.br) ? bf16_bits_to_f32(f.br[e]) : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kFLogitsPerThread; ++j) {
+            const int i = tid + j * kGuWaves * 64;
+            if (i >= T * E) continue;
+            const int t = i / E, e = i - t * E;
             float v = 0.f;
 #pragma unroll
-            for (int ks = 0; ks < kLogitSlices; ++ks) v += f.part[((size_t)ks * T + t) * E + e];
-            if (f.br) v += bf16_bits_to_f32(f.br[e]);
-            sl[i] = v;
-            key = order_key(v, e);
+            for (int ks = 0; ks < kLogitSlices; ++ks) v += pv[j][ks];
+            v += bv[j];
+            sl[t * kFMaxE + e] = v;
+            skey[t * kFMaxE + e] = order_key(v, e);
             if (writer && f.logits) f.logits[(size_t)t * E + e] = v;
         }
-        skey[i] = key;
     }
     __syncthreads();
 
@@ -452,22 +486,13 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
         const bool ok = lane < E;
         const unsigned long long mine = skey[t * kFMaxE + lane];
         const float v = sl[t * kFMaxE + lane];
-        int rank = 0;
         const u32x4* krow = reinterpret_cast<const u32x4*>(skey + t * kFMaxE);
-#pragma unroll
-        for (int c = 0; c < kFMaxE / 2; ++c) {  // two keys per 16-byte read
-            const u32x4 q = krow[c];
-            const unsigned long long k0 = ((unsigned long long)q.y << 32) | q.x;
-            const unsigned long long k1 = ((unsigned long long)q.w << 32) | q.z;
-            rank += (k0 > mine ? 1 : 0) + (k1 > mine ? 1 : 0);
-        }
+        const int rank = E <= 32 ? rank_of<16>(krow, mine) : rank_of<32>(krow, mine);
         const bool chosen = ok & (rank < k);
         const uint64_t top = __ballot(ok & (rank == 0));
         const float smax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__builtin_ctzll(top)));
         const float z = chosen ? expf(v - smax) : 0.f;
-        float zs = z;  // butterfly sum: every lane adds the same pairs, so all get the same value
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) zs += __shfl_xor(zs, d, 64);
+        const float zs = wave_sum(z);
         const uint64_t bal = __ballot(chosen);
         const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
         const int pos = __popcll(bal & lt);  // ascending expert order

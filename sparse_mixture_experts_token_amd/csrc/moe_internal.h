@@ -121,6 +121,35 @@ __device__ __forceinline__ void decode_mxfp4_32(const u32x4& q, uint32_t scale, 
     }
 }
 
+// ------------------------------------------------------- cross-lane helpers --
+// Moves within 16-lane rows (DPP): no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
+
+__device__ __forceinline__ float lane_f(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// Wave-wide sum in a fixed order; the result is the same in every lane (each
+// step adds a pair of lanes that both end with the same value).
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);
+    x += dpp_f<kDppMirror>(x);
+    return ((lane_f(x, 0) + lane_f(x, 16)) + lane_f(x, 32)) + lane_f(x, 48);
+}
+
 // -------------------------------------------------------------- top-k order --
 // 64-bit key of logit v of expert e: the value mapped to an order-preserving
 // unsigned integer (NaN lowest, -0 as +0) above the complement of the index,

@@ -52,22 +52,6 @@ __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_t* p, size_t
 
 constexpr int kNone = 0x7fffffff;
 
-// Cross-lane moves within 16-lane rows (DPP): no LDS round trip.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int x) {
-    return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xf, 0xf, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __int_as_float(dpp_i<CTRL>(__float_as_int(x)));
-}
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
-constexpr int kDppHalfMirror = 0x141; // lane i <- 7 - i within 8
-constexpr int kDppMirror = 0x140;     // lane i <- 15 - i within 16
-
-__device__ __forceinline__ float lane_f(float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); }
-
 // (value, index) order: larger value wins, then lower index.  A lane without
 // a candidate holds index kNone; any candidate beats it, so a candidate is
 // always found while one exists (even for NaN or -inf logits).
@@ -95,15 +79,6 @@ __device__ __forceinline__ void wave_argmax(float& v, int& idx) {
     for (int r = 1; r < 4; ++r) argmax_merge(bv, bi, lane_f(v, 16 * r), __builtin_amdgcn_readlane(idx, 16 * r));
     v = bv;
     idx = bi;
-}
-
-// Wave-wide sum in a fixed order; the result is the same in every lane.
-__device__ __forceinline__ float wave_sum(float x) {
-    x += dpp_f<kDppXor1>(x);
-    x += dpp_f<kDppXor2>(x);
-    x += dpp_f<kDppHalfMirror>(x);
-    x += dpp_f<kDppMirror>(x);
-    return ((lane_f(x, 0) + lane_f(x, 16)) + lane_f(x, 32)) + lane_f(x, 48);
 }
 
 // One pass over K for CB 16-wide expert column blocks starting at cb0.
