@@ -481,27 +481,66 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
     }
     __syncthreads();
 
-    // 2. top-k by rank + softmax over the selected set, one token per wave
-    for (int t = wave; t < T; t += kGuWaves) {
-        const bool ok = lane < E;
-        const unsigned long long mine = skey[t * kFMaxE + lane];
-        const float v = sl[t * kFMaxE + lane];
-        const u32x4* krow = reinterpret_cast<const u32x4*>(skey + t * kFMaxE);
-        const int rank = E <= 32 ? rank_of<16>(krow, mine) : rank_of<32>(krow, mine);
-        const bool chosen = ok & (rank < k);
-        const uint64_t top = __ballot(ok & (rank == 0));
-        const float smax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), (int)__builtin_ctzll(top)));
-        const float z = chosen ? expf(v - smax) : 0.f;
-        const float zs = wave_sum(z);
-        const uint64_t bal = __ballot(chosen);
-        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        const int pos = __popcll(bal & lt);  // ascending expert order
-        if (chosen) {
-            ti[t * k + pos] = lane;
-            atomicOr(&emask[lane], 1ull << t);
-            if (writer) {
-                f.topk_idx[(size_t)t * k + pos] = lane;
-                f.topk_w[(size_t)t * k + pos] = z / zs;
+    // 2. top-k by rank + softmax over the selected set: with E <= 32 a wave
+    //    takes two tokens at once (lanes 0..31 and 32..63), else one
+    if (E <= 32) {
+        const int half = lane >> 5, le = lane & 31;
+        for (int tp = 2 * wave; tp < T; tp += 2 * kGuWaves) {
+            const int t = tp + half;
+            const bool tv = t < T;  // an odd last pair has no second token
+            const int trow = tv ? t : tp;
+            const bool ok = tv & (le < E);
+            const unsigned long long mine = skey[trow * kFMaxE + le];
+            const float v = sl[trow * kFMaxE + le];
+            const int rank = rank_of<16>(reinterpret_cast<const u32x4*>(skey + trow * kFMaxE), mine);
+            const bool chosen = ok & (rank < k);
+            const uint64_t top = __ballot(ok & (rank == 0));
+            const uint32_t top0 = (uint32_t)top, top1 = (uint32_t)(top >> 32);
+            const float m0 = lane_f(v, top0 ? (int)__builtin_ctz(top0) : 0);
+            const float m1 = lane_f(v, top1 ? 32 + (int)__builtin_ctz(top1) : 32);
+            const float z = chosen ? expf(v - (half ? m1 : m0)) : 0.f;
+            // 16-lane row sums (DPP), then rows 0+1 and rows 2+3: the same
+            // order as the one-token sum, whose rows 2 and 3 hold zeros here
+            float x = z;
+            x += dpp_f<kDppXor1>(x);
+            x += dpp_f<kDppXor2>(x);
+            x += dpp_f<kDppHalfMirror>(x);
+            x += dpp_f<kDppMirror>(x);
+            const float zs = half ? lane_f(x, 32) + lane_f(x, 48) : lane_f(x, 0) + lane_f(x, 16);
+            const uint64_t bal = __ballot(chosen);
+            const uint32_t balh = half ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+            const uint32_t lt = le == 0 ? 0u : (~0u >> (32 - le));
+            const int pos = __popc(balh & lt);  // ascending expert order
+            if (chosen) {
+                ti[t * k + pos] = le;
+                atomicOr(&emask[le], 1ull << t);
+                if (writer) {
+                    f.topk_idx[(size_t)t * k + pos] = le;
+                    f.topk_w[(size_t)t * k + pos] = z / zs;
+                }
+            }
+        }
+    } else {
+        for (int t = wave; t < T; t += kGuWaves) {
+            const bool ok = lane < E;
+            const unsigned long long mine = skey[t * kFMaxE + lane];
+            const float v = sl[t * kFMaxE + lane];
+            const int rank = rank_of<32>(reinterpret_cast<const u32x4*>(skey + t * kFMaxE), mine);
+            const bool chosen = ok & (rank < k);
+            const uint64_t top = __ballot(ok & (rank == 0));
+            const float smax = lane_f(v, (int)__builtin_ctzll(top));
+            const float z = chosen ? expf(v - smax) : 0.f;
+            const float zs = wave_sum(z);
+            const uint64_t bal = __ballot(chosen);
+            const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            const int pos = __popcll(bal & lt);  // ascending expert order
+            if (chosen) {
+                ti[t * k + pos] = lane;
+                atomicOr(&emask[lane], 1ull << t);
+                if (writer) {
+                    f.topk_idx[(size_t)t * k + pos] = lane;
+                    f.topk_w[(size_t)t * k + pos] = z / zs;
+                }
             }
         }
     }
