@@ -412,24 +412,6 @@ __host__ __device__ inline FLayout flayout(int T, int k, int max_tiles) {
     return L;
 }
 
-// Number of the 2 NC keys at krow that exceed `mine`.  All reads are issued
-// before the first compare (a data-dependent exit between them would make
-// every read wait out its own latency).
-template <int NC>
-__device__ __forceinline__ int rank_of(const u32x4* krow, unsigned long long mine) {
-    u32x4 q[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) q[c] = krow[c];
-    int rank = 0;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const unsigned long long k0 = ((unsigned long long)q[c].y << 32) | q[c].x;
-        const unsigned long long k1 = ((unsigned long long)q[c].w << 32) | q[c].z;
-        rank += (k0 > mine ? 1 : 0) + (k1 > mine ? 1 : 0);
-    }
-    return rank;
-}
-
 template <int WDT>
 __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArgs f) {
     extern __shared__ __align__(16) unsigned char smem[];

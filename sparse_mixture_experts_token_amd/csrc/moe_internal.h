@@ -162,6 +162,24 @@ __device__ __forceinline__ unsigned long long order_key(float v, int e) {
     return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)e);
 }
 
+// Number of the 2 NC keys at krow (LDS) that exceed `mine`.  All reads are
+// issued before the first compare (a data-dependent exit between them would
+// make every read wait out its own latency).
+template <int NC>
+__device__ __forceinline__ int rank_of(const u32x4* krow, unsigned long long mine) {
+    u32x4 q[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) q[c] = krow[c];
+    int rank = 0;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const unsigned long long k0 = ((unsigned long long)q[c].y << 32) | q[c].x;
+        const unsigned long long k1 = ((unsigned long long)q[c].w << 32) | q[c].z;
+        rank += (k0 > mine ? 1 : 0) + (k1 > mine ? 1 : 0);
+    }
+    return rank;
+}
+
 // ------------------------------------------------------------- MFMA wrappers --
 // 32x32x16 bf16: lane l holds A[l%32][8(l/32)+0..7], B[8(l/32)+0..7][l%32];
 // D[4i+j] is row 8i+4(l/32)+j, column l%32.

@@ -21,7 +21,8 @@ namespace moe {
 namespace {
 
 constexpr int kBaseLds = 16384;  // ints of scanned bases kept in LDS (64 KB)
-constexpr int kPer = 4;           // elements per lane per round of loads
+constexpr int kPer = 4;           // elements per lane per round of loads (per-expert scans)
+constexpr int kScatterPer = 16;   // assignments per thread per round of loads (scatter)
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -145,18 +146,18 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     }
 
     // 4. stable scatter: row = offsets[e] + (earlier tiles' count) + rank in tile.
-    //    Loads of kPer assignments are issued together.
+    //    Loads of kScatterPer assignments are issued together.
     const int total = T * k;
-    for (int a0 = 0; a0 < total; a0 += 1024 * kPer) {
-        int e[kPer], lr[kPer];
+    for (int a0 = 0; a0 < total; a0 += 1024 * kScatterPer) {
+        int e[kScatterPer], lr[kScatterPer];
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
+        for (int j = 0; j < kScatterPer; ++j) {
             const int a = a0 + j * 1024 + tid;
             e[j] = a < total ? topk_idx[a] : 0;
             lr[j] = a < total ? local_rank[a] : 0;
         }
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
+        for (int j = 0; j < kScatterPer; ++j) {
             const int a = a0 + j * 1024 + tid;
             if (a < total) {
                 const int b = (a / k) / kRouterTokens;

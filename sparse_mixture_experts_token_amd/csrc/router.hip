@@ -40,7 +40,9 @@ struct RouterSmem {
         const size_t sel = (size_t)BT * Ep * 2;
         return part_off(Ep) + (sel > part_bytes() ? sel : part_bytes());
     }
-    static __host__ __device__ size_t bytes(int Ep) { return bias_off(Ep) + (size_t)Ep * 4; }
+    // order keys [BT][64] u64 (one expert per lane only)
+    static __host__ __device__ size_t key_off(int Ep) { return bias_off(Ep) + (size_t)Ep * 4; }
+    static __host__ __device__ size_t bytes(int Ep) { return key_off(Ep) + (Ep == 64 ? (size_t)BT * 64 * 8 : 0); }
 };
 
 template <typename TA>
@@ -155,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
     float* part = reinterpret_cast<float*>(smem + RouterSmem::part_off(Ep));
     uint16_t* selpos = reinterpret_cast<uint16_t*>(smem + RouterSmem::selpos_off(Ep));
     float* s_bias = reinterpret_cast<float*>(smem + RouterSmem::bias_off(Ep));
+    unsigned long long* skey = reinterpret_cast<unsigned long long*>(smem + RouterSmem::key_off(Ep));
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -224,28 +227,24 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
 
     // -------------------------------------------- top-k + selected softmax --
     if constexpr (NV == 1) {
-        // one expert per lane: selection by rank.  Expert e is chosen when
-        // fewer than k experts have a larger order key (value, then lower
-        // index); positions are in ascending expert order.
+        // one expert per lane: selection by rank.  Every logit gets its order
+        // key once (value, then lower index; 0 past E); expert e is chosen when
+        // fewer than k keys exceed its own.  Positions are in ascending
+        // expert order.
+        for (int i = tid; i < BT * 64; i += kThreads) {
+            const int e = i & 63;
+            skey[i] = (e < E && t0 + (i >> 6) < T) ? order_key(s_lds[i], e) : 0ull;
+        }
+        __syncthreads();
         for (int tt = wave; tt < BT; tt += NW) {
             const int t = t0 + tt;
             if (t >= T) break;  // wave-uniform
             const bool ok = lane < E;
             const float v = ok ? s_lds[tt * Ep + lane] : 0.f;
-            const unsigned long long mine = ok ? order_key(v, lane) : 0ull;
-            const f32x4* row = reinterpret_cast<const f32x4*>(s_lds + tt * Ep);
-            int rank = 0;
-            for (int c0 = 0; c0 < 16; c0 += 4) {  // four 16-byte reads at a time
-#pragma unroll
-                for (int c = c0; c < c0 + 4; ++c) {
-                    const f32x4 q = row[c];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int e2 = 4 * c + j;
-                        rank += ((e2 < E) & (order_key(q[j], e2) > mine)) ? 1 : 0;
-                    }
-                }
-            }
+            const unsigned long long mine = skey[tt * 64 + lane];
+            const u32x4* krow = reinterpret_cast<const u32x4*>(skey + tt * 64);
+            int rank = rank_of<16>(krow, mine);             // experts 0..31
+            if (E > 32) rank += rank_of<16>(krow + 16, mine);  // 32..63 (two batches fit the registers)
             if (logits_opt && ok) logits_opt[(size_t)t * E + lane] = v;
             const bool chosen = ok & (rank < k);
             const uint64_t top = __ballot(ok & (rank == 0));
