@@ -101,7 +101,9 @@ struct Batch {
     u32x4 b[4];
 };
 
-template <int MODE, int WDT, int NP>
+// With SL the MXFP4 scales are not loaded here: scales_fetch() reads them from
+// the copy scales_load()/scales_store() put in LDS.
+template <int MODE, int WDT, int NP, bool SL = false>
 __device__ __forceinline__ void issue(Batch<MODE, WDT, NP>& x, buf_rsrc w0, buf_rsrc w1, buf_rsrc s0, buf_rsrc s1,
                                       buf_rsrc bsrc, const uint32_t (&n)[NP], const bool (&nv)[NP],
                                       uint32_t b_base, bool has_row, uint32_t K, uint32_t g, uint32_t qd) {
@@ -112,10 +114,10 @@ __device__ __forceinline__ void issue(Batch<MODE, WDT, NP>& x, buf_rsrc w0, buf_
             const bool kv = nv[p] && kq < K;
             const uint32_t co = kv ? n[p] * (K / 2) + kq / 2 : kOob, so = kv ? n[p] * (K / 32) + kq / 32 : kOob;
             x.wq[p] = buf_load16(w0, co, 0);
-            x.ws[p] = buf_load1(s0, so, 0);
+            if constexpr (!SL) x.ws[p] = buf_load1(s0, so, 0);
             if constexpr (MODE == 0) {
                 x.uq[p] = buf_load16(w1, co, 0);
-                x.us[p] = buf_load1(s1, so, 0);
+                if constexpr (!SL) x.us[p] = buf_load1(s1, so, 0);
             }
         } else {
 #pragma unroll
@@ -169,13 +171,72 @@ __device__ __forceinline__ void compute(const Batch<MODE, WDT, NP>& x, f32x4 (&a
     }
 }
 
+// MXFP4 scales of one block, staged in LDS: the 16 rows of a panel keep their
+// K/32 scale bytes contiguous in memory, so a few 4-byte-per-lane loads fetch
+// a panel's scales for the whole contraction, instead of one 1-byte load per
+// K step (whose per-instruction cost dominated the decode kernels).  Layout:
+// [panel][matrix][16 rows][K/32] bytes.
+constexpr int kScaleDw = 10;                           // dwords per lane per panel-matrix
+constexpr uint32_t kScaleMaxKg = kScaleDw * 64 * 4 / 16;  // largest K/32 staged: 160 (MXFP4 layers: K <= 4992)
+
+template <int NP, int NMAT>
+struct ScaleStage {
+    uint32_t v[NP * NMAT][kScaleDw];
+};
+
+template <int NP, int NMAT>
+__device__ __forceinline__ void scales_load(ScaleStage<NP, NMAT>& st, buf_rsrc s0, buf_rsrc s1, uint32_t c0,
+                                            uint32_t KG, int lane) {
+    const uint32_t seg = 16 * KG;
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int m = 0; m < NMAT; ++m) {
+            const uint32_t base = (c0 + 16 * p) * KG;  // rows past N read past the buffer: 0
+#pragma unroll
+            for (int j = 0; j < kScaleDw; ++j) {
+                const uint32_t off = (uint32_t)(lane * 4 + j * 256);
+                st.v[p * NMAT + m][j] =
+                    off < seg ? __builtin_amdgcn_raw_buffer_load_b32(m ? s1 : s0, base + off, 0, 0) : 0u;
+            }
+        }
+}
+
+template <int NP, int NMAT>
+__device__ __forceinline__ void scales_store(const ScaleStage<NP, NMAT>& st, uint8_t* sl, uint32_t KG, int lane) {
+    const uint32_t seg = 16 * KG;
+#pragma unroll
+    for (int pm = 0; pm < NP * NMAT; ++pm)
+#pragma unroll
+        for (int j = 0; j < kScaleDw; ++j) {
+            const uint32_t off = (uint32_t)(lane * 4 + j * 256);
+            if (off < seg) *reinterpret_cast<uint32_t*>(sl + pm * seg + off) = st.v[pm][j];
+        }
+}
+
+// Scales of K step g for this lane from the LDS copy (0 past K or past the
+// block, where the codes read as zeros: a NaN scale must not meet them).
+template <int MODE, int WDT, int NP>
+__device__ __forceinline__ void scales_fetch(Batch<MODE, WDT, NP>& x, const uint8_t* sl, const bool (&nv)[NP],
+                                             uint32_t KG, uint32_t g, int r, uint32_t qd) {
+    constexpr int NMAT = MODE == 0 ? 2 : 1;
+    const uint32_t grp = 4 * g + qd, seg = 16 * KG;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const bool kv = nv[p] && grp < KG;
+        const uint32_t o = (uint32_t)(p * NMAT) * seg + (uint32_t)r * KG + grp;
+        x.ws[p] = kv ? sl[o] : 0u;
+        if constexpr (MODE == 0) x.us[p] = kv ? sl[o + seg] : 0u;
+    }
+}
+
 // One block: weight rows [c0, c1) (c1 - c0 <= 16 NP, both multiples of four)
 // of the expert of `tile` against the tile's activation rows; perm holds the
 // assignment of every expert-major row (global memory or LDS).  DEPTH = K
 // steps of loads in flight (1 or 2).
-template <int MODE, int WDT, int DEPTH, int NP = kPanels>
+template <int MODE, int WDT, int DEPTH, int NP = kPanels, bool SL = false>
 __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, const int32_t* perm, uint32_t c0,
-                                            uint32_t c1, int lane) {
+                                            uint32_t c1, int lane, uint8_t* sl = nullptr) {
     const int e = tile.expert, row0 = tile.row_start, rows = tile.rows;
     const uint32_t K = (uint32_t)a.K, N = (uint32_t)a.N;
     const int r = lane & 15;
@@ -218,7 +279,29 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
     // Steps past the end read beyond K: zeros, no memory traffic.
     const uint32_t ng = (K + 127) / 128;
     Batch<MODE, WDT, NP> x0, x1;
-    if constexpr (DEPTH == 1) {
+    constexpr bool kSL = SL && WDT == DT_MXFP4;
+    const uint32_t KG = K / 32;
+    if constexpr (kSL) {
+        // scales of the whole block into LDS; their loads go out first and the
+        // first K step's code loads overlap their latency
+        static_assert(DEPTH == 2, "staged scales: two K steps in flight");
+        ScaleStage<NP, MODE == 0 ? 2 : 1> st;
+        scales_load<NP, MODE == 0 ? 2 : 1>(st, s0, s1, c0, KG, lane);
+        issue<MODE, WDT, NP, true>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, 0, qd);
+        scales_store<NP, MODE == 0 ? 2 : 1>(st, sl, KG, lane);
+        for (uint32_t g = 0; g < ng; g += 2) {
+            issue<MODE, WDT, NP, true>(x1, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 1, qd);
+            __builtin_amdgcn_sched_barrier(0);
+            scales_fetch<MODE, WDT, NP>(x0, sl, nv, KG, g, r, qd);
+            compute<MODE, WDT, NP>(x0, acc0, acc1);
+            __builtin_amdgcn_sched_barrier(0);
+            issue<MODE, WDT, NP, true>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 2, qd);
+            __builtin_amdgcn_sched_barrier(0);
+            scales_fetch<MODE, WDT, NP>(x1, sl, nv, KG, g + 1, r, qd);
+            compute<MODE, WDT, NP>(x1, acc0, acc1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else if constexpr (DEPTH == 1) {
         for (uint32_t g = 0; g < ng; ++g) {
             issue<MODE, WDT, NP>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g, qd);
             __builtin_amdgcn_sched_barrier(0);
@@ -301,8 +384,8 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_balanced_kernel(DArgs a)
 }
 
 // One block of 16 NP weight rows per wave: wave q takes block q % nb of tile
-// q / nb, nb = ceil(N / (16 NP)).
-template <int MODE, int WDT, int DEPTH, int NP>
+// q / nb, nb = ceil(N / (16 NP)).  SL: MXFP4 scales staged in LDS (K/32 <= kScaleMaxKg).
+template <int MODE, int WDT, int DEPTH, int NP, bool SL>
 __global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int ntl = min(a.n_tiles[0], a.max_tiles);
@@ -312,7 +395,10 @@ __global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
     const int mt = q / ncb, cb = q - mt * ncb;
     if (mt >= ntl) return;  // wave-uniform; this kernel has no barriers
     const uint32_t c0 = (uint32_t)cb * kRows;
-    decode_pass<MODE, WDT, DEPTH, NP>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane);
+    extern __shared__ __align__(16) unsigned char dsm[];  // SL: the block's scales (one wave per workgroup)
+    static_assert(!SL || kBlkWaves == 1, "staged scales are per wave");
+    decode_pass<MODE, WDT, DEPTH, NP, SL>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane,
+                                          dsm);
 }
 
 // ------------------------------------------------ fused routing + gate/up --
@@ -636,7 +722,12 @@ hipError_t launch_blocks(const GemmProblem& p, hipStream_t stream) {
     const DArgs a = make_dargs(p, MODE);
     const size_t ncb = ((size_t)a.N + 16 * NP - 1) / (16 * NP);
     const int blocks = (int)(((size_t)p.max_tiles * ncb + kBlkWaves - 1) / kBlkWaves);
-    decode_block_kernel<MODE, WDT, DEPTH, NP><<<blocks, kBlkWaves * 64, 0, stream>>>(a);
+    // MXFP4: the block's scales in LDS, [panel][matrix][16][K/32] bytes
+    constexpr bool kSL = WDT == DT_MXFP4;
+    static_assert(!kSL || DEPTH == 2, "staged scales: two K steps in flight");
+    if (kSL && (uint32_t)a.K / 32 > kScaleMaxKg) return hipErrorInvalidValue;  // beyond the MXFP4 K limit
+    const size_t smem = kSL ? (size_t)NP * (MODE == 0 ? 2 : 1) * 16 * (a.K / 32) : 0;
+    decode_block_kernel<MODE, WDT, DEPTH, NP, kSL><<<blocks, kBlkWaves * 64, smem, stream>>>(a);
     return hipGetLastError();
 }
 

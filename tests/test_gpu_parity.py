@@ -72,6 +72,10 @@ EDGE = [
     # routing computed inside the gate/up kernel (T <= 64, E <= 64): its largest shape and one expert
     synth.Config(114, "decode-fused-64-tokens-64-experts", T=64, H=256, I=128, E=64, k=16, act="bf16", expert="bf16"),
     synth.Config(115, "decode-fused-single-expert", T=16, H=64, I=64, E=1, k=1, act="bf16", expert="bf16"),
+    # MXFP4 decode with the scales staged in LDS (E > 64, so not fused): K tails in both products;
+    # then the largest MXFP4 K (4992, 156 scale groups per row)
+    synth.Config(116, "decode-mxfp4-staged-scales", T=24, H=192, I=320, E=80, k=2, act="bf16", expert="mxfp4"),
+    synth.Config(117, "decode-mxfp4-max-K", T=4, H=4992, I=64, E=66, k=1, act="bf16", expert="mxfp4"),
 ]
 
 
