@@ -102,7 +102,7 @@ struct Batch {
 };
 
 // With SL the MXFP4 scales are not loaded here: scales_fetch() reads them from
-// the copy scales_load()/scales_store() put in LDS.
+// the copy scales_dma() put in LDS.
 template <int MODE, int WDT, int NP, bool SL = false>
 __device__ __forceinline__ void issue(Batch<MODE, WDT, NP>& x, buf_rsrc w0, buf_rsrc w1, buf_rsrc s0, buf_rsrc s1,
                                       buf_rsrc bsrc, const uint32_t (&n)[NP], const bool (&nv)[NP],
@@ -172,45 +172,30 @@ __device__ __forceinline__ void compute(const Batch<MODE, WDT, NP>& x, f32x4 (&a
 }
 
 // MXFP4 scales of one block, staged in LDS: the 16 rows of a panel keep their
-// K/32 scale bytes contiguous in memory, so a few 4-byte-per-lane loads fetch
-// a panel's scales for the whole contraction, instead of one 1-byte load per
-// K step (whose per-instruction cost dominated the decode kernels).  Layout:
-// [panel][matrix][16 rows][K/32] bytes.
-constexpr int kScaleDw = 10;                           // dwords per lane per panel-matrix
-constexpr uint32_t kScaleMaxKg = kScaleDw * 64 * 4 / 16;  // largest K/32 staged: 160 (MXFP4 layers: K <= 4992)
+// K/32 scale bytes contiguous in memory, so a few 4-byte-per-lane loads copy a
+// panel's scales for the whole contraction straight into LDS (no registers),
+// instead of one 1-byte load per K step (whose per-instruction cost dominated
+// the decode kernels).  Layout: [panel][matrix] segments of nj 256-byte lines,
+// nj = ceil(16 K/32 / 256), row r of a panel at byte r K/32 of its segment; a
+// lane's dword past the panel's bytes lands in its own segment's padding.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr uint32_t kScaleMaxKg = 160;  // largest K/32 staged (MXFP4 layers: K <= 4992)
+
+__host__ __device__ constexpr uint32_t scale_lines(uint32_t KG) { return (16 * KG + 255) / 256; }
 
 template <int NP, int NMAT>
-struct ScaleStage {
-    uint32_t v[NP * NMAT][kScaleDw];
-};
-
-template <int NP, int NMAT>
-__device__ __forceinline__ void scales_load(ScaleStage<NP, NMAT>& st, buf_rsrc s0, buf_rsrc s1, uint32_t c0,
-                                            uint32_t KG, int lane) {
-    const uint32_t seg = 16 * KG;
+__device__ __forceinline__ void scales_dma(buf_rsrc s0, buf_rsrc s1, uint32_t c0, uint32_t KG, uint8_t* sl,
+                                           int lane) {
+    const uint32_t nj = scale_lines(KG);
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int m = 0; m < NMAT; ++m) {
             const uint32_t base = (c0 + 16 * p) * KG;  // rows past N read past the buffer: 0
-#pragma unroll
-            for (int j = 0; j < kScaleDw; ++j) {
-                const uint32_t off = (uint32_t)(lane * 4 + j * 256);
-                st.v[p * NMAT + m][j] =
-                    off < seg ? __builtin_amdgcn_raw_buffer_load_b32(m ? s1 : s0, base + off, 0, 0) : 0u;
-            }
-        }
-}
-
-template <int NP, int NMAT>
-__device__ __forceinline__ void scales_store(const ScaleStage<NP, NMAT>& st, uint8_t* sl, uint32_t KG, int lane) {
-    const uint32_t seg = 16 * KG;
-#pragma unroll
-    for (int pm = 0; pm < NP * NMAT; ++pm)
-#pragma unroll
-        for (int j = 0; j < kScaleDw; ++j) {
-            const uint32_t off = (uint32_t)(lane * 4 + j * 256);
-            if (off < seg) *reinterpret_cast<uint32_t*>(sl + pm * seg + off) = st.v[pm][j];
+            uint8_t* seg = sl + (p * NMAT + m) * nj * 256;
+            for (uint32_t j = 0; j < nj; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(m ? s1 : s0, (lds_void*)(seg + j * 256), 4,
+                                                         base + j * 256 + (uint32_t)lane * 4, 0, 0, 0);
         }
 }
 
@@ -220,7 +205,7 @@ template <int MODE, int WDT, int NP>
 __device__ __forceinline__ void scales_fetch(Batch<MODE, WDT, NP>& x, const uint8_t* sl, const bool (&nv)[NP],
                                              uint32_t KG, uint32_t g, int r, uint32_t qd) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
-    const uint32_t grp = 4 * g + qd, seg = 16 * KG;
+    const uint32_t grp = 4 * g + qd, seg = scale_lines(KG) * 256;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const bool kv = nv[p] && grp < KG;
@@ -285,10 +270,15 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
         // scales of the whole block into LDS; their loads go out first and the
         // first K step's code loads overlap their latency
         static_assert(DEPTH == 2, "staged scales: two K steps in flight");
-        ScaleStage<NP, MODE == 0 ? 2 : 1> st;
-        scales_load<NP, MODE == 0 ? 2 : 1>(st, s0, s1, c0, KG, lane);
+        constexpr int NMAT = MODE == 0 ? 2 : 1;
+        scales_dma<NP, NMAT>(s0, s1, c0, KG, sl, lane);
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
         issue<MODE, WDT, NP, true>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, 0, qd);
-        scales_store<NP, MODE == 0 ? 2 : 1>(st, sl, KG, lane);
+        // The compiler does not track the LDS writes of the copies above.  Loads
+        // retire in issue order and the first step issued NP NMAT + 4 after them,
+        // so once at most NP NMAT remain outstanding the scales are in LDS.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP * NMAT) : "memory");
         for (uint32_t g = 0; g < ng; g += 2) {
             issue<MODE, WDT, NP, true>(x1, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 1, qd);
             __builtin_amdgcn_sched_barrier(0);
@@ -726,7 +716,7 @@ hipError_t launch_blocks(const GemmProblem& p, hipStream_t stream) {
     constexpr bool kSL = WDT == DT_MXFP4;
     static_assert(!kSL || DEPTH == 2, "staged scales: two K steps in flight");
     if (kSL && (uint32_t)a.K / 32 > kScaleMaxKg) return hipErrorInvalidValue;  // beyond the MXFP4 K limit
-    const size_t smem = kSL ? (size_t)NP * (MODE == 0 ? 2 : 1) * 16 * (a.K / 32) : 0;
+    const size_t smem = kSL ? (size_t)NP * (MODE == 0 ? 2 : 1) * scale_lines(a.K / 32) * 256 : 0;
     decode_block_kernel<MODE, WDT, DEPTH, NP, kSL><<<blocks, kBlkWaves * 64, smem, stream>>>(a);
     return hipGetLastError();
 }
