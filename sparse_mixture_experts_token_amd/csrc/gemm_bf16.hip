@@ -337,13 +337,35 @@ __device__ __forceinline__ void main_loop(const ItemCtx<C>& x, unsigned char* sm
     stage_iter<C, BN, MB, false, false, 0>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
 }
 
-// Main loop for the MB live row groups of this wave (MB = 1 .. MBW; a wave
-// with none computes one group from a valid row and discards it).
+// A wave with no live row group (the short last tile of an expert) still
+// fills its share of every stage and meets every barrier of main_loop (one
+// before the loop, one per stage that has a successor), but reads and
+// multiplies nothing, which leaves its SIMD to the wave it shares it with.
+template <class C>
+__device__ __forceinline__ void dma_only_loop(const ItemCtx<C>& x, unsigned char* smem, int nk, int wave) {
+    wait_stages_ahead<C::DPS>(min(nk, C::NST) - 1);
+    wait_lds_reads();  // MXFP4: this wave's scale writes
+    bare_barrier();
+    int kt = 0;
+    for (; kt + C::NST < nk; ++kt) {
+        wait_vmcnt<(C::NST - 2) * C::DPS>();
+        bare_barrier();
+        dma_stage<C>(x.src, smem, kt + C::NST, wave, x.a_voff, x.b_voff, x.b_mat);
+    }
+    for (; kt + 1 < nk; ++kt) {
+        wait_stages_ahead<C::DPS>(min(nk - 1, kt + C::NST - 1) - (kt + 1));
+        bare_barrier();
+    }
+}
+
+// Main loop for the MB live row groups of this wave (MB = 1 .. MBW), or the
+// DMA-only loop for a wave with none.
 template <class C, int BN, int MB>
 __device__ __forceinline__ void dispatch_mb(int mine, const ItemCtx<C>& x, unsigned char* smem, int nk, int wave,
                                             int lane, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
     if constexpr (MB == 1) {
-        main_loop<C, BN, 1>(x, smem, nk, wave, lane, acc);
+        if (mine >= 1) main_loop<C, BN, 1>(x, smem, nk, wave, lane, acc);
+        else dma_only_loop<C>(x, smem, nk, wave);
     } else {
         if (mine >= MB) main_loop<C, BN, MB>(x, smem, nk, wave, lane, acc);
         else dispatch_mb<C, BN, MB - 1>(mine, x, smem, nk, wave, lane, acc);
