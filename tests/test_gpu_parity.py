@@ -162,6 +162,53 @@ def test_silent_expansion_identity(M):
     print({"M": M, "gpu_vs_gpu_rel_l2": r})
 
 
+@pytest.mark.parametrize("M,kp", [(2, 4), (3, 4), (2, 2)], ids=["64a4", "96a4", "64a2"])
+def test_silent_expansion_narrow_k(M, kp):
+    """Deploy-narrow shapes: the 32a4 layer expanded M times, run with k' = kp
+    at T = 256.  Copies of a router row give bitwise-equal logits, so where
+    the k'-th pick is one of several copies (96a4: three copies of the best
+    expert and one of the second) the lower index must win exactly as in the
+    reference.  Routing bit-exact and outputs within tolerance against the
+    fp64 reference on the expanded layer; where kp = M j the expanded GPU
+    layer also matches the base GPU layer at top-j."""
+    L, st = layer_full(2)
+    c = L.cfg
+    T = 256
+    base = problem(c, T)
+    w = device_weights(L, st)
+    wx = {n: torch.empty((M * t.shape[0],) + tuple(t.shape[1:]), dtype=t.dtype, device=t.device)
+          for n, t in w.items()}
+    smoe.moe_expand_silent(base, w, M, wx)
+    big = smoe.Problem(T, c.H, c.I, M * c.E, kp, base.act_dtype, base.expert_dtype)
+    h = to_dev(L.h[:T], "bf16")
+    gx = run(big, wx, h, "bf16")
+    ow = oracle_weights(L, st)
+    cmap = np.arange(M * c.E) % c.E
+    wr = oracle.expand_silent(ow.w_router, M, cmap)
+    br = oracle.expand_silent(ow.b_router, M, cmap)
+    owx = oracle.LayerWeights(wr, br, lambda j: ow.expert(cmap[j]))
+    h64 = oracle.widen(L.h[:T], "bf16")
+    # distinct base experts near a selection boundary would make the pick
+    # legitimately ambiguous; this draw has none among any token's top three
+    sb = -np.sort(-oracle.router_logits(h64, ow.w_router, ow.b_router), axis=1)
+    j = -(-kp // M)
+    assert np.min(sb[:, :j] - sb[:, 1:j + 1]) >= 1e-5
+    s = oracle.router_logits(h64, wr, br)
+    ref_idx = oracle.select_topk(s, kp)
+    np.testing.assert_array_equal(gx["topk_idx"], ref_idx)
+    md = oracle.routing_metadata(ref_idx, M * c.E)
+    np.testing.assert_array_equal(gx["expert_offsets"], md["offsets"])
+    np.testing.assert_array_equal(gx["perm_src"], md["perm_src"])
+    ref = oracle.moe_forward(h64, owx, kp, idx=ref_idx, workers=workers())
+    m = check_out(gx["out"], ref["out"], "bf16")
+    if kp % M == 0:
+        gb = run(problem(c, T, k=kp // M), w, h, "bf16")
+        r = rel_l2(gx["out"], gb["out"])
+        assert r <= 5e-3 and np.abs(gx["out"] - gb["out"]).max() <= 1e-2 * np.abs(gb["out"]).max()
+        m["gpu_vs_base_top_j"] = r
+    print(m)
+
+
 def test_random_64a8_prefill_4096_sampled():
     L, st = layer_full(3)
     m, _ = check_layer(L, st, tokens=sample_tokens(L.T, 128, 3))

@@ -252,6 +252,30 @@ def test_silent_init_identity(M):
                                        oracle.moe_forward(h, w, j)["out"], rtol=1e-12, atol=1e-14)
 
 
+def test_expansion_with_k_not_a_multiple_of_M():
+    """Three copies of every expert, k' = 4: the selection is the three copies
+    of the best expert and the lowest copy of the second (exact ties go to the
+    lower index), so the layer is the closed form
+    (3 e1 y1 + e2 y2) / (3 e1 + e2), e_i = exp(s_i - s_1), y_i = expert i's output."""
+    rng = np.random.default_rng(41)
+    E, M = 8, 3
+    h, w, ex = rand_layer(rng, T=40, H=24, I=40, E=E)
+    big = oracle.moe_forward(h, _expanded(w, ex, M), 4)
+    s = h @ w.w_router.T + w.b_router
+    order = np.argsort(-s, axis=1, kind="stable")
+    for t in range(len(h)):
+        b1, b2 = order[t, 0], order[t, 1]
+        np.testing.assert_array_equal(big["idx"][t], sorted([b1, b1 + E, b1 + 2 * E, b2]))
+        ys = []
+        for b in (b1, b2):
+            wg, wu, wd = ex[b]
+            g, u = wg @ h[t], wu @ h[t]
+            ys.append(wd @ (g / (1 + np.exp(-g)) * u))
+        e2 = np.exp(s[t, b2] - s[t, b1])
+        want = (3 * ys[0] + e2 * ys[1]) / (3 + e2)
+        np.testing.assert_allclose(big["out"][t], want, rtol=1e-12, atol=1e-15)
+
+
 def test_silent_identity_fixture_weights():
     L = synth.make_layer(1)
     w = oracle.LayerWeights.from_storage("f32", "f32", L.w_router, L.b_router, L.expert)
