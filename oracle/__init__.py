@@ -21,6 +21,8 @@ Sources (web pages; cited by title and section):
   Section 5.2: original experts keep indices 0..E-1, copies follow.
 * "gpt-oss 20B" field guide, cutaway 03 "Sparse Mixture of Experts": SwiGLU
   experts, top four of 32, the selected scores normalised, weighted sum.
+  Cutaway 04 "One decoder block": RMSNorm before the MoE sublayer, whose
+  output is added back to the residual stream.
 * "openai/gpt-oss-20b" fixture comparison page, Preserved properties and
   Config changes tables: ``hidden_act = silu``; the fixture shape.
 * "gpt-oss-20b and gpt-oss-120b" explainer, "Four-bit expert weights": MXFP4
@@ -45,10 +47,12 @@ from .moe import (
     expand_silent,
     LayerWeights,
 )
+from .block import rms_norm, block_forward, block_forward_per_token
 
 __all__ = [
     "e2m1_value", "e8m0_value", "mxfp4_dequant", "mxfp4_bits_per_param",
     "widen", "router_logits", "select_topk", "topk_gap", "selected_softmax",
     "silu", "swiglu_expert", "moe_forward", "moe_forward_per_token",
     "routing_metadata", "expand_silent", "LayerWeights",
+    "rms_norm", "block_forward", "block_forward_per_token",
 ]

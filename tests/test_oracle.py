@@ -431,3 +431,69 @@ def test_parameter_counts_match_three_HxI_matrices_per_expert():
     assert round(with_bias / 1e9, 1) == g["layers_B"]
     assert round(emb / 1e6, 1) == g["embed_M"] == g["lm_head_M"]
     assert round(H / 1e3, 1) == g["norm_K"]
+
+
+# ------------------------------------------- pre-norm and residual add --
+
+def test_rms_norm_unit_mean_square():
+    """Unit gain, epsilon 0: every output row has mean square exactly 1."""
+    x = np.random.default_rng(50).standard_normal((7, 33)) * 3.0
+    n = oracle.rms_norm(x, np.ones(33), 0.0)
+    np.testing.assert_allclose(np.mean(n * n, axis=1), 1.0, rtol=1e-14)
+
+
+def test_rms_norm_constant_row_closed_form():
+    """A row of c's: the mean square is c^2, so each element is g c / sqrt(c^2 + eps)."""
+    g = np.linspace(0.5, 2.0, 16)
+    for c, eps in ((2.0, 0.0), (-0.3, 1e-5), (1e-3, 1e-5), (5.0, 0.25)):
+        n = oracle.rms_norm(np.full((1, 16), c), g, eps)
+        np.testing.assert_allclose(n[0], g * c / np.sqrt(c * c + eps), rtol=1e-15)
+
+
+def test_rms_norm_joint_scaling_of_input_and_eps():
+    """rms_norm(a x; a^2 eps) = rms_norm(x; eps) for a > 0 (epsilon sits inside
+    the square root, in units of the mean square)."""
+    rng = np.random.default_rng(51)
+    x, g = rng.standard_normal((5, 24)), rng.standard_normal(24)
+    for a in (1e-3, 0.5, 7.0):
+        np.testing.assert_allclose(oracle.rms_norm(a * x, g, a * a * 1e-4), oracle.rms_norm(x, g, 1e-4),
+                                   rtol=1e-13, atol=1e-15)
+
+
+def test_rms_norm_gain_acts_per_feature():
+    """The gain scales features (columns), not tokens: T != H so a transposed
+    gain could not broadcast silently."""
+    rng = np.random.default_rng(52)
+    x, g = rng.standard_normal((3, 8)), rng.standard_normal(8)
+    base = oracle.rms_norm(x, np.ones(8), 1e-6)
+    np.testing.assert_allclose(oracle.rms_norm(x, g, 1e-6), base * g[None, :], rtol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.rms_norm(x, np.ones(3), 1e-6)
+
+
+def test_rms_norm_hand_example():
+    """x = (3, 4), unit gain, eps = 0: mean square 12.5, so (3, 4) / sqrt(12.5)."""
+    n = oracle.rms_norm(np.array([[3.0, 4.0]]), np.ones(2), 0.0)
+    np.testing.assert_allclose(n[0], [0.8485281374238570, 1.1313708498984760], rtol=1e-15)
+
+
+def test_block_zero_experts_is_identity():
+    """Zero down projections: every expert outputs 0, so the block returns its input."""
+    rng = np.random.default_rng(53)
+    h, w, ex = rand_layer(rng, T=20, H=24, I=40, E=6)
+    zex = [(wg, wu, np.zeros_like(wd)) for wg, wu, wd in ex]
+    wz = oracle.LayerWeights(w.w_router, w.b_router, lambda e: zex[e])
+    out = oracle.block_forward(h, rng.standard_normal(24), 1e-5, wz, 2)["out"]
+    np.testing.assert_array_equal(out, h)
+
+
+def test_block_two_evaluations_agree():
+    """Expert-grouped evaluation vs token-by-token loops (mean square summed
+    element by element, experts by matrix-vector products)."""
+    rng = np.random.default_rng(54)
+    h, w, ex = rand_layer(rng, T=24, H=16, I=20, E=5)
+    g = rng.uniform(0.5, 1.5, 16)
+    for k in (1, 2, 5):
+        a = oracle.block_forward(h, g, 1e-5, w, k)["out"]
+        b = oracle.block_forward_per_token(h, g, 1e-5, w, k)
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
