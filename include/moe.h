@@ -139,6 +139,30 @@ int moe_forward(const moe_problem *p, const moe_weights *w, const void *h, void 
                 const moe_routing *routing, void *workspace, size_t workspace_bytes,
                 void *stream);
 
+/* The pre-normalised MoE sublayer of a decoder block with its residual add
+ * ("gpt-oss 20B" field guide, cutaway 04 "One decoder block": RMSNorm before
+ * the MoE sublayer, whose output is added back to the residual stream; the
+ * "openai/gpt-oss-20b" fixture page's parameter table: one gain per hidden
+ * feature, no bias):
+ *     out = x + MoE(n),   n = norm_weight * x / sqrt(mean(x^2) + eps)
+ * per token, mean over the H features.  x, out and norm_weight [H] are in
+ * act_dtype; MoE is the layer of moe_forward with weights *w.
+ * Arithmetic: the mean square and the scale in fp32.  The router works on
+ * (norm_weight * x) * scale in fp32 (so routing follows the normalised input
+ * to fp32 precision, not a rounded copy); with bf16 activations the expert
+ * GEMMs take n rounded once to bf16.  The residual is added in fp32 to the
+ * sum of the expert outputs before the single rounding of out.
+ * Deterministic.  `workspace` must hold moe_block_workspace_bytes(p) bytes;
+ * out must not overlap x.  `routing` as in moe_forward (logits are those of
+ * the normalised input).  Profiling stage 0 includes the normalisation.
+ * Errors: as moe_forward (x in the place of h), plus MOE_ERR_NULL for
+ * norm_weight, MOE_ERR_ALIGN for norm_weight not 16-byte aligned and
+ * MOE_ERR_SHAPE for eps negative, NaN or infinite. */
+size_t moe_block_workspace_bytes(const moe_problem *p);
+int moe_block_forward(const moe_problem *p, const moe_weights *w, const void *norm_weight, float eps,
+                      const void *x, void *out, const moe_routing *routing, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Silent expansion ("gpt-oss-40b-64a8-init" page, section 2 Principle/Proof,
  * section 5.2): for every per-expert tensor of *src (w_router, b_router,
  * w_gate, w_up, w_down and, for MXFP4, the three scale tensors) write

@@ -10,6 +10,8 @@ The functions mirror the C entry points of ``include/moe.h``:
 
 * ``moe_workspace_bytes(problem)``
 * ``moe_forward(problem, weights, h, out, routing=None, workspace=None)``
+* ``moe_block_workspace_bytes(problem)``
+* ``moe_block_forward(problem, weights, norm_weight, eps, x, out, routing=None, workspace=None)``
 * ``moe_expand_silent(base, src, M, dst)``
 * ``moe_status_string(status)``
 * ``moe_profile_begin(max_calls)`` / ``moe_profile_begin_mask(max_calls, mask)`` / ``moe_profile_end()``
@@ -34,7 +36,8 @@ MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
 MOE_NUM_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_HIP", -7: "MOE_ERR_STATE"}
-EXPORTED = ("moe_workspace_bytes", "moe_forward", "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
+EXPORTED = ("moe_workspace_bytes", "moe_forward", "moe_block_workspace_bytes", "moe_block_forward",
+            "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
             "moe_profile_begin", "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name")
 MOE_PROFILE_ALL = (1 << (MOE_NUM_STAGES + 1)) - 1
 
@@ -93,6 +96,12 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.POINTER(_Routing), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_block_workspace_bytes.argtypes = [ctypes.POINTER(_Problem)]
+    lib.moe_block_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_block_forward.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_void_p,
+                                      ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_expand_silent.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_int32,
                                       ctypes.POINTER(_Weights), ctypes.c_void_p]
     lib.moe_expand_silent.restype = ctypes.c_int
@@ -156,6 +165,25 @@ def moe_workspace_bytes(problem: Problem) -> int:
     return int(load().moe_workspace_bytes(ctypes.byref(p)))
 
 
+def _routing(routing: dict | None):
+    if routing is None:
+        return None
+    unknown = set(routing) - set(_ROUTING_FIELDS)
+    if unknown:
+        raise KeyError(f"unknown routing fields {sorted(unknown)}")
+    return _Routing(*[_ptr(routing.get(n)) for n in _ROUTING_FIELDS])
+
+
+def _workspace(size_fn, p, like, workspace, workspace_bytes):
+    if workspace is None:
+        nbytes = int(size_fn(ctypes.byref(p)))
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=like.device if like is not None else "cuda")
+        return workspace, nbytes
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    return workspace, workspace_bytes
+
+
 def moe_forward(problem: Problem, weights: dict, h, out, routing: dict | None = None, workspace=None,
                 workspace_bytes: int | None = None, stream=None) -> None:
     """Enqueue the layer on ``stream`` (default: torch's current stream).
@@ -163,21 +191,32 @@ def moe_forward(problem: Problem, weights: dict, h, out, routing: dict | None = 
     lib = load()
     p = problem._c()
     w = _weights(weights)
-    r = None
-    if routing is not None:
-        unknown = set(routing) - set(_ROUTING_FIELDS)
-        if unknown:
-            raise KeyError(f"unknown routing fields {sorted(unknown)}")
-        r = _Routing(*[_ptr(routing.get(n)) for n in _ROUTING_FIELDS])
-    if workspace is None:
-        nbytes = int(lib.moe_workspace_bytes(ctypes.byref(p)))
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=h.device if h is not None else "cuda")
-        workspace_bytes = nbytes
-    elif workspace_bytes is None:
-        workspace_bytes = workspace.numel() * workspace.element_size()
+    r = _routing(routing)
+    workspace, workspace_bytes = _workspace(lib.moe_workspace_bytes, p, h, workspace, workspace_bytes)
     st = lib.moe_forward(ctypes.byref(p), ctypes.byref(w), _ptr(h), _ptr(out),
                          ctypes.byref(r) if r is not None else None, _ptr(workspace), int(workspace_bytes),
                          _stream(stream))
+    _check(st)
+
+
+def moe_block_workspace_bytes(problem: Problem) -> int:
+    p = problem._c()
+    return int(load().moe_block_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_block_forward(problem: Problem, weights: dict, norm_weight, eps: float, x, out,
+                      routing: dict | None = None, workspace=None, workspace_bytes: int | None = None,
+                      stream=None) -> None:
+    """Enqueue ``out = x + MoE(RMSNorm(x))`` on ``stream`` (default: torch's
+    current stream); ``norm_weight`` is the [H] gain in the activation format."""
+    lib = load()
+    p = problem._c()
+    w = _weights(weights)
+    r = _routing(routing)
+    workspace, workspace_bytes = _workspace(lib.moe_block_workspace_bytes, p, x, workspace, workspace_bytes)
+    st = lib.moe_block_forward(ctypes.byref(p), ctypes.byref(w), _ptr(norm_weight), float(eps), _ptr(x), _ptr(out),
+                               ctypes.byref(r) if r is not None else None, _ptr(workspace), int(workspace_bytes),
+                               _stream(stream))
     _check(st)
 
 

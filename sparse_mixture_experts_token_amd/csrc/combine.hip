@@ -3,7 +3,10 @@
 // The down stage already multiplied each expert output by its weight p_i and
 // stored it at the assignment's slot, so
 //     out[t, :] = y[t*k + 0, :] + y[t*k + 1, :] + ... + y[t*k + k-1, :]
-// summed in fp32 in slot order (= ascending expert id), rounded once.
+// summed in fp32 in slot order (= ascending expert id), rounded once.  In the
+// pre-normalised block the residual-stream row x[t, :] is added to that sum
+// before the rounding ("gpt-oss 20B" field guide, cutaway 04: each sublayer
+// is added back to the residual stream).
 // Memory bound: 4 outputs per thread, 16-byte loads.
 #include "moe_internal.h"
 
@@ -12,7 +15,7 @@ namespace {
 
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, void* __restrict__ out, int T,
-                                                      int H, int k) {
+                                                      int H, int k, const void* __restrict__ residual) {
     const int h4 = H >> 2;
     const size_t n4 = (size_t)T * h4;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
@@ -27,6 +30,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
             acc.z += v.z;
             acc.w += v.w;
         }
+        if (residual) {
+            if constexpr (kBf16Out) {
+                const uint2 r = reinterpret_cast<const uint2*>(residual)[i];
+                acc.x += bf16_bits_to_f32(r.x & 0xffffu);
+                acc.y += bf16_bits_to_f32(r.x >> 16);
+                acc.z += bf16_bits_to_f32(r.y & 0xffffu);
+                acc.w += bf16_bits_to_f32(r.y >> 16);
+            } else {
+                const float4 r = reinterpret_cast<const float4*>(residual)[i];
+                acc.x += r.x;
+                acc.y += r.y;
+                acc.z += r.z;
+                acc.w += r.w;
+            }
+        }
         if constexpr (kBf16Out) {
             uint2 o;
             o.x = f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16);
@@ -40,13 +58,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k, hipStream_t stream) {
+hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k, const void* residual,
+                          hipStream_t stream) {
     const size_t n4 = (size_t)T * (H / 4);
     const int blocks = (int)((n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192);
     if (act_dtype == DT_BF16)
-        combine_kernel<true><<<blocks, 256, 0, stream>>>(y, out, T, H, k);
+        combine_kernel<true><<<blocks, 256, 0, stream>>>(y, out, T, H, k, residual);
     else
-        combine_kernel<false><<<blocks, 256, 0, stream>>>(y, out, T, H, k);
+        combine_kernel<false><<<blocks, 256, 0, stream>>>(y, out, T, H, k, residual);
     return hipGetLastError();
 }
 

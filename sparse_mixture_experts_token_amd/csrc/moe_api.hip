@@ -1,6 +1,7 @@
 // C interface of the sparse MoE layer (declared in include/moe.h): argument
-// checks, workspace layout, stage launches on the caller's stream, the silent
-// expansion and the per-stage timing hooks.
+// checks, workspace layout, stage launches on the caller's stream, the
+// pre-normalised block entry point, the silent expansion and the per-stage
+// timing hooks.
 #include <mutex>
 #include <vector>
 
@@ -46,12 +47,15 @@ struct Layout {
     bool lists;  // prefill work lists are built
 };
 
-Layout layout(const moe_problem* p) {
+// router_dt: the router's input format (-1: the activation format).  The
+// partial-logits kernel and the fused decode routing take bf16 input only.
+Layout layout(const moe_problem* p, int router_dt = -1) {
     Layout L{};
+    const int rdt = router_dt < 0 ? p->act_dtype : router_dt;
     const size_t tk = (size_t)p->T * p->k;
     L.decode = moe::decode_path(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
-    L.fused = moe::decode_fused(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
-    L.plogits = p->act_dtype == MOE_BF16 && p->T <= 64;
+    L.fused = rdt == MOE_BF16 && moe::decode_fused(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
+    L.plogits = rdt == MOE_BF16 && p->T <= 64;
     L.BM = L.decode ? moe::decode_block_m() : moe::gemm_block_m(p->act_dtype, p->expert_dtype, p->T, p->k, p->E);
     L.nblk = (p->T + moe::kRouterTokens - 1) / moe::kRouterTokens;
     L.max_tiles = (int)((tk + L.BM - 1) / L.BM) + p->E;
@@ -80,6 +84,28 @@ Layout layout(const moe_problem* p) {
     return L;
 }
 
+// The block entry point's workspace: the layer's, then the normalised input
+// in fp32 (the router's input; also the GEMMs' for fp32 activations) and, for
+// bf16 activations, in bf16 (the GEMMs' input) and the router widened to fp32.
+struct BlockLayout {
+    Layout L;
+    size_t n32, n16, wr32, br32, total;
+};
+
+BlockLayout block_layout(const moe_problem* p) {
+    BlockLayout B{};
+    B.L = layout(p, MOE_F32);
+    const size_t th = (size_t)p->T * p->H;
+    const bool bf = p->act_dtype == MOE_BF16;
+    size_t o = B.L.total;
+    B.n32 = o;  o = align_up(o + th * 4);
+    B.n16 = o;  o = align_up(o + (bf ? th * 2 : 0));
+    B.wr32 = o; o = align_up(o + (bf ? (size_t)p->E * p->H * 4 : 0));
+    B.br32 = o; o = align_up(o + (bf ? (size_t)p->E * 4 : 0));
+    B.total = o;
+    return B;
+}
+
 // ------------------------------------------------------------ profiling --
 struct Profiler {
     std::mutex mu;
@@ -104,6 +130,136 @@ hipEvent_t* prof_slot(uint32_t* mask) {
     return &P.ev[(size_t)(P.used++) * (MOE_NUM_STAGES + 1)];
 }
 
+// Checks shared by the forward entry points (h is the layer input).  T = 0
+// sets *noop: nothing to do, outputs untouched.
+int check_call(const moe_problem* p, const moe_weights* w, const void* h, const void* out,
+               const moe_routing* routing, const void* workspace, bool* noop) {
+    *noop = false;
+    int st = check_problem(p);
+    if (st != MOE_OK) return st;
+    if (!w) return MOE_ERR_NULL;
+    if (p->T == 0) {
+        *noop = true;
+        return MOE_OK;
+    }
+    if (!h || !out || !workspace || !w->w_router || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
+    if (p->expert_dtype == MOE_MXFP4 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL;
+    for (const void* q : {h, (const void*)out, (const void*)workspace, w->w_router, w->w_gate, w->w_up, w->w_down})
+        if (!aligned(q, 16)) return MOE_ERR_ALIGN;
+    if (w->b_router && !aligned(w->b_router, act_bytes(p->act_dtype))) return MOE_ERR_ALIGN;
+    if (routing) {
+        for (const void* q : {(const void*)routing->logits, (const void*)routing->topk_idx,
+                              (const void*)routing->topk_w, (const void*)routing->expert_offsets,
+                              (const void*)routing->perm_src})
+            if (q && !aligned(q, 4)) return MOE_ERR_ALIGN;
+    }
+    return MOE_OK;
+}
+
+// Inputs of one pass through the stages besides the problem, the expert
+// weights and the outputs.
+struct PassIn {
+    int router_dt;         // format of router_h, w_router and b_router
+    const void* router_h;  // the router's input [T, H]
+    const void* w_router;
+    const void* b_router;  // may be null
+    const void* gemm_h;    // the expert GEMMs' input [T, H] (act dtype)
+    const void* residual;  // added in the combine (act dtype) or null
+    // pre-norm prologue (norm_g null: none), writing n32 / n16 / wr32 / br32
+    const void* norm_g;
+    float eps;
+    const void* x;
+    float* n32;
+    uint16_t* n16;
+    float* wr32;
+    float* br32;
+};
+
+int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void* out, const moe_routing* routing,
+             char* ws, const Layout& L, hipStream_t stream) {
+    int32_t* topk_idx = (routing && routing->topk_idx) ? routing->topk_idx : (int32_t*)(ws + L.topk_idx);
+    float* topk_w = (routing && routing->topk_w) ? routing->topk_w : (float*)(ws + L.topk_w);
+    int32_t* offsets = (routing && routing->expert_offsets) ? routing->expert_offsets : (int32_t*)(ws + L.offsets);
+    int32_t* perm = (routing && routing->perm_src) ? routing->perm_src : (int32_t*)(ws + L.perm);
+    float* logits = routing ? routing->logits : nullptr;
+    int32_t* blk = (int32_t*)(ws + L.blk);
+    int32_t* rank = (int32_t*)(ws + L.rank);
+    int32_t* inv = (int32_t*)(ws + L.inv);
+    Tile* tiles = (Tile*)(ws + L.tiles);
+    int32_t* ntiles = (int32_t*)(ws + L.ntiles);
+    void* act = ws + L.act;
+    float* y = (float*)(ws + L.y);
+
+    uint32_t ev_mask = 0;
+    hipEvent_t* ev = prof_slot(&ev_mask);
+    auto mark = [&](int i) {
+        if (ev && ((ev_mask >> i) & 1u)) (void)hipEventRecord(ev[i], stream);
+    };
+
+    hipError_t e = hipSuccess;
+    moe::WorkList wl0{L.lists ? (int32_t*)(ws + L.work0) : nullptr, ntiles + 1, L.nc0};
+    moe::WorkList wl1{L.lists ? (int32_t*)(ws + L.work1) : nullptr, ntiles + 2, L.nc1};
+    int32_t* queues = (int32_t*)(ws + L.queues);
+    float* part = (float*)(ws + L.part);
+    mark(0);
+    if (in.norm_g) {
+        e = moe::launch_rms_norm(p->act_dtype, in.x, in.norm_g, in.eps, p->T, p->H, in.n32, in.n16, w->w_router,
+                                 w->b_router, p->E, in.wr32, in.br32, stream);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (L.plogits) {
+        e = moe::launch_decode_logits(in.router_h, in.w_router, p->T, p->H, p->E, part, stream);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    if (!L.fused) {
+        e = moe::launch_router(in.router_dt, in.router_h, in.w_router, in.b_router, p->T, p->H, p->E, p->k, logits,
+                               topk_idx, topk_w, blk, rank, L.plogits ? part : nullptr, stream);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    mark(1);
+    if (!L.fused) {
+        e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
+                                   L.max_tiles, wl0, wl1, queues, moe::kNumQueues, stream);
+        if (e != hipSuccess) return MOE_ERR_HIP;
+    }
+    mark(2);
+
+    moe::GemmProblem g{};
+    g.T = p->T; g.H = p->H; g.I = p->I; g.E = p->E; g.k = p->k;
+    g.act_dtype = p->act_dtype;
+    g.expert_dtype = p->expert_dtype;
+    g.h = in.gemm_h;
+    g.w_gate = w->w_gate; g.w_up = w->w_up; g.w_down = w->w_down;
+    g.s_gate = w->s_gate; g.s_up = w->s_up; g.s_down = w->s_down;
+    g.perm_src = perm;
+    g.topk_w = topk_w;
+    g.tiles = tiles;
+    g.n_tiles = ntiles;
+    g.max_tiles = L.max_tiles;
+    g.work_gateup = wl0.items;
+    g.n_work_gateup = wl0.count;
+    g.work_down = wl1.items;
+    g.n_work_down = wl1.count;
+    g.act = act;
+    g.y = y;
+    g.decode = L.decode;
+    g.queues = queues;
+    if (L.fused) {
+        const moe::FusedRouting fr{part, in.b_router, logits, topk_idx, topk_w, offsets, perm, inv, tiles, ntiles};
+        e = moe::launch_route_gateup_decode(g, fr, stream);
+    } else {
+        e = moe::launch_gateup(g, stream);
+    }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(3);
+    e = moe::launch_down(g, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(4);
+    e = moe::launch_combine(p->act_dtype, y, out, p->T, p->H, p->k, in.residual, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(5);
+    return MOE_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -135,103 +291,54 @@ const char* moe_stage_name(int s) {
 
 int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void* out, const moe_routing* routing,
                 void* workspace, size_t workspace_bytes, void* stream_v) {
-    int st = check_problem(p);
-    if (st != MOE_OK) return st;
-    if (!w) return MOE_ERR_NULL;
-    if (p->T == 0) return MOE_OK;
-    if (!h || !out || !workspace || !w->w_router || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_NULL;
-    if (p->expert_dtype == MOE_MXFP4 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_NULL;
-    for (const void* q : {h, (const void*)out, (const void*)workspace, w->w_router, w->w_gate, w->w_up, w->w_down})
-        if (!aligned(q, 16)) return MOE_ERR_ALIGN;
-    if (w->b_router && !aligned(w->b_router, act_bytes(p->act_dtype))) return MOE_ERR_ALIGN;
-    if (routing) {
-        for (const void* q : {(const void*)routing->logits, (const void*)routing->topk_idx,
-                              (const void*)routing->topk_w, (const void*)routing->expert_offsets,
-                              (const void*)routing->perm_src})
-            if (q && !aligned(q, 4)) return MOE_ERR_ALIGN;
-    }
+    bool noop = false;
+    const int st = check_call(p, w, h, out, routing, workspace, &noop);
+    if (st != MOE_OK || noop) return st;
     const Layout L = layout(p);
     if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+    PassIn in{};
+    in.router_dt = p->act_dtype;
+    in.router_h = h;
+    in.w_router = w->w_router;
+    in.b_router = w->b_router;
+    in.gemm_h = h;
+    return run_pass(p, w, in, out, routing, reinterpret_cast<char*>(workspace), L,
+                    reinterpret_cast<hipStream_t>(stream_v));
+}
 
-    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+size_t moe_block_workspace_bytes(const moe_problem* p) {
+    if (check_problem(p) != MOE_OK) return 0;
+    return block_layout(p).total;
+}
+
+int moe_block_forward(const moe_problem* p, const moe_weights* w, const void* norm_weight, float eps, const void* x,
+                      void* out, const moe_routing* routing, void* workspace, size_t workspace_bytes,
+                      void* stream_v) {
+    bool noop = false;
+    const int st = check_call(p, w, x, out, routing, workspace, &noop);
+    if (st != MOE_OK || noop) return st;
+    if (!norm_weight) return MOE_ERR_NULL;
+    if (!aligned(norm_weight, 16)) return MOE_ERR_ALIGN;
+    if (!(eps >= 0.0f) || eps > 1e30f) return MOE_ERR_SHAPE;  // also rejects NaN and inf
+    const BlockLayout B = block_layout(p);
+    if (workspace_bytes < B.total) return MOE_ERR_WORKSPACE;
     char* ws = reinterpret_cast<char*>(workspace);
-    int32_t* topk_idx = (routing && routing->topk_idx) ? routing->topk_idx : (int32_t*)(ws + L.topk_idx);
-    float* topk_w = (routing && routing->topk_w) ? routing->topk_w : (float*)(ws + L.topk_w);
-    int32_t* offsets = (routing && routing->expert_offsets) ? routing->expert_offsets : (int32_t*)(ws + L.offsets);
-    int32_t* perm = (routing && routing->perm_src) ? routing->perm_src : (int32_t*)(ws + L.perm);
-    float* logits = routing ? routing->logits : nullptr;
-    int32_t* blk = (int32_t*)(ws + L.blk);
-    int32_t* rank = (int32_t*)(ws + L.rank);
-    int32_t* inv = (int32_t*)(ws + L.inv);
-    Tile* tiles = (Tile*)(ws + L.tiles);
-    int32_t* ntiles = (int32_t*)(ws + L.ntiles);
-    void* act = ws + L.act;
-    float* y = (float*)(ws + L.y);
-
-    uint32_t ev_mask = 0;
-    hipEvent_t* ev = prof_slot(&ev_mask);
-    auto mark = [&](int i) {
-        if (ev && ((ev_mask >> i) & 1u)) (void)hipEventRecord(ev[i], stream);
-    };
-
-    hipError_t e = hipSuccess;
-    moe::WorkList wl0{L.lists ? (int32_t*)(ws + L.work0) : nullptr, ntiles + 1, L.nc0};
-    moe::WorkList wl1{L.lists ? (int32_t*)(ws + L.work1) : nullptr, ntiles + 2, L.nc1};
-    int32_t* queues = (int32_t*)(ws + L.queues);
-    float* part = (float*)(ws + L.part);
-    mark(0);
-    if (L.plogits) {
-        e = moe::launch_decode_logits(h, w->w_router, p->T, p->H, p->E, part, stream);
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    if (!L.fused) {
-        e = moe::launch_router(p->act_dtype, h, w->w_router, w->b_router, p->T, p->H, p->E, p->k, logits, topk_idx,
-                               topk_w, blk, rank, L.plogits ? part : nullptr, stream);
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    mark(1);
-    if (!L.fused) {
-        e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
-                                   L.max_tiles, wl0, wl1, queues, moe::kNumQueues, stream);
-        if (e != hipSuccess) return MOE_ERR_HIP;
-    }
-    mark(2);
-
-    moe::GemmProblem g{};
-    g.T = p->T; g.H = p->H; g.I = p->I; g.E = p->E; g.k = p->k;
-    g.act_dtype = p->act_dtype;
-    g.expert_dtype = p->expert_dtype;
-    g.h = h;
-    g.w_gate = w->w_gate; g.w_up = w->w_up; g.w_down = w->w_down;
-    g.s_gate = w->s_gate; g.s_up = w->s_up; g.s_down = w->s_down;
-    g.perm_src = perm;
-    g.topk_w = topk_w;
-    g.tiles = tiles;
-    g.n_tiles = ntiles;
-    g.max_tiles = L.max_tiles;
-    g.work_gateup = wl0.items;
-    g.n_work_gateup = wl0.count;
-    g.work_down = wl1.items;
-    g.n_work_down = wl1.count;
-    g.act = act;
-    g.y = y;
-    g.decode = L.decode;
-    g.queues = queues;
-    if (L.fused) {
-        const moe::FusedRouting fr{part, w->b_router, logits, topk_idx, topk_w, offsets, perm, inv, tiles, ntiles};
-        e = moe::launch_route_gateup_decode(g, fr, stream);
-    } else {
-        e = moe::launch_gateup(g, stream);
-    }
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    mark(3);
-    e = moe::launch_down(g, stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    mark(4);
-    e = moe::launch_combine(p->act_dtype, y, out, p->T, p->H, p->k, stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-    mark(5);
-    return MOE_OK;
+    const bool bf = p->act_dtype == MOE_BF16;
+    PassIn in{};
+    in.norm_g = norm_weight;
+    in.eps = eps;
+    in.x = x;
+    in.n32 = (float*)(ws + B.n32);
+    in.n16 = bf ? (uint16_t*)(ws + B.n16) : nullptr;
+    in.wr32 = bf ? (float*)(ws + B.wr32) : nullptr;
+    in.br32 = bf ? (float*)(ws + B.br32) : nullptr;
+    in.router_dt = MOE_F32;  // logits from the fp32 normalised input
+    in.router_h = in.n32;
+    in.w_router = bf ? (const void*)in.wr32 : w->w_router;
+    in.b_router = bf ? (w->b_router ? (const void*)in.br32 : nullptr) : w->b_router;
+    in.gemm_h = bf ? (const void*)in.n16 : (const void*)in.n32;
+    in.residual = x;
+    return run_pass(p, w, in, out, routing, ws, B.L, reinterpret_cast<hipStream_t>(stream_v));
 }
 
 int moe_expand_silent(const moe_problem* base, const moe_weights* src, int32_t M, const moe_weights* dst,

@@ -292,8 +292,16 @@ int mxfp4_max_k();                   // largest H or I the MXFP4 kernels take
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down(const GemmProblem& p, hipStream_t stream);
 
-// Stage 4: out[t] = sum_slot y[t*k+slot] (fp32, slot order), rounded to act dtype.
-hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k,
+// Stage 4: out[t] = sum_slot y[t*k+slot] (fp32, slot order) [+ residual[t]],
+// rounded to act dtype.  residual (act dtype, [T, H]) may be null.
+hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k, const void* residual,
                           hipStream_t stream);
+
+// Block prologue: n32 = g * x / sqrt(mean(x^2) + eps) in fp32 [T, H], and for
+// bf16 activations n16 = n32 rounded to bf16 plus the router widened to fp32
+// (wr32 [E, H], br32 [E] when b_router is not null).
+hipError_t launch_rms_norm(int act_dtype, const void* x, const void* g, float eps, int T, int H, float* n32,
+                           uint16_t* n16, const void* w_router, const void* b_router, int E, float* wr32,
+                           float* br32, hipStream_t stream);
 
 }  // namespace moe

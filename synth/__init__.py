@@ -36,7 +36,7 @@ import numpy as np
 ROOT_SEED = 20261203
 
 # tensor ids of the per-tensor streams
-TID_H, TID_WR, TID_BR, TID_GATE, TID_UP, TID_DOWN, TID_HOT = range(7)
+TID_H, TID_WR, TID_BR, TID_GATE, TID_UP, TID_DOWN, TID_HOT, TID_ROWSCALE, TID_NORM = range(9)
 
 
 @dataclass(frozen=True)
@@ -225,6 +225,22 @@ def make_layer(key, T: int | None = None, hot_beta: float | None = None) -> Laye
         br32[hot] += np.float32(beta)
     return Layer(cfg=c, T=T, h=_store(h32, c.act), w_router=_store(wr32, c.act),
                  b_router=_store(br32, c.act), hot_set=hot)
+
+
+def block_inputs(layer: Layer) -> tuple[np.ndarray, np.ndarray]:
+    """Inputs of the pre-normalised block built on ``layer``, in the
+    activation format: the residual stream ``x`` (``h`` with each row scaled
+    by a seeded factor drawn log-uniformly from [0.5, 2], so rows differ in
+    mean square) and the norm gain ``g`` ``[H]`` drawn uniformly from
+    [0.5, 1.5]."""
+    c = layer.cfg
+    scale = np.exp2(rng_for(c.cid, TID_ROWSCALE).uniform(-1.0, 1.0, c.T).astype(np.float32))[:layer.T]
+    if c.act == "bf16":
+        h32 = (np.asarray(layer.h, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    else:
+        h32 = np.asarray(layer.h, dtype=np.float32)
+    g32 = rng_for(c.cid, TID_NORM).uniform(0.5, 1.5, c.H).astype(np.float32)
+    return _store(h32 * scale[:, None], c.act), _store(g32, c.act)
 
 
 def decode_T(key: int) -> int:

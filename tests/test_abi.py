@@ -20,7 +20,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = smoe.load()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(smoe.EXPORTED) == names
@@ -76,6 +76,31 @@ def test_forward_argument_errors_return_before_any_launch():
     assert _call(mx, weights=w) == -1
     # T = 0 is a no-op even with no buffers at all
     assert _call(smoe.Problem(0, 64, 128, 4, 2, smoe.MOE_F32, smoe.MOE_F32), h=0, out=0, ws=0, ws_bytes=0) == 0
+
+
+def _block(problem, g=0x5000, eps=1e-5, x=0x1000, out=0x2000, ws=0x3000, ws_bytes=1 << 40):
+    lib = smoe.load()
+    w = smoe._Weights(*[0x4000 for _ in smoe._WEIGHT_FIELDS])
+    p = problem._c()
+    return lib.moe_block_forward(ctypes.byref(p), ctypes.byref(w), g, eps, x, out, None, ws, ws_bytes, None)
+
+
+def test_block_argument_errors_return_before_any_launch():
+    P = smoe.Problem(16, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_BF16)
+    lib = smoe.load()
+    need = lib.moe_block_workspace_bytes(ctypes.byref(P._c()))
+    # the normalised input (fp32 and bf16) and the widened router come on top of the routing tables
+    assert need > lib.moe_workspace_bytes(ctypes.byref(P._c())) > 0
+    assert _block(P, g=0) == -1
+    assert _block(P, g=0x5004) == -5
+    assert _block(P, x=0) == -1
+    for eps in (-1e-6, float("nan"), float("inf")):
+        assert _block(P, eps=eps) == -2, eps
+    assert _block(P, ws_bytes=need - 1) == -4
+    assert _block(smoe.Problem(16, 64, 128, 4, 5, smoe.MOE_BF16, smoe.MOE_BF16)) == -2
+    # T = 0 is a no-op even with no buffers at all
+    assert _block(smoe.Problem(0, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_BF16), g=0, x=0, out=0, ws=0,
+                  ws_bytes=0) == 0
 
 
 def test_expand_and_decode_argument_errors():
