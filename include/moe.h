@@ -147,11 +147,13 @@ int moe_forward(const moe_problem *p, const moe_weights *w, const void *h, void 
  *     out = x + MoE(n),   n = norm_weight * x / sqrt(mean(x^2) + eps)
  * per token, mean over the H features.  x, out and norm_weight [H] are in
  * act_dtype; MoE is the layer of moe_forward with weights *w.
- * Arithmetic: the mean square and the scale in fp32.  The router works on
- * (norm_weight * x) * scale in fp32 (so routing follows the normalised input
- * to fp32 precision, not a rounded copy); with bf16 activations the expert
- * GEMMs take n rounded once to bf16.  The residual is added in fp32 to the
- * sum of the expert outputs before the single rounding of out.
+ * Arithmetic: the mean square and the scale in fp32.  Routing follows the
+ * normalised input to fp32 precision, not a rounded copy: the logits are
+ * scale * (x . (W_r * norm_weight)) + b_r with x taken exactly (bf16: the
+ * folded router split exactly into two bf16 parts; fp32: the fp32 router on
+ * the fp32 normalised input).  With bf16 activations the expert GEMMs take n
+ * rounded once to bf16.  The residual is added in fp32 to the sum of the
+ * expert outputs before the single rounding of out.
  * Deterministic.  `workspace` must hold moe_block_workspace_bytes(p) bytes;
  * out must not overlap x.  `routing` as in moe_forward (logits are those of
  * the normalised input).  Profiling stage 0 includes the normalisation.

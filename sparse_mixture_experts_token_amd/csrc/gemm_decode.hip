@@ -418,38 +418,54 @@ constexpr int kFMaxE = 64;        // experts (one per lane in top-k)
 constexpr int kLogitSteps = 12;   // 32-wide K steps per batch of loads in the logits kernel
 constexpr int kFLogitsPerThread = (kFMaxT * kFMaxE + kGuWaves * 64 - 1) / (kGuWaves * 64);
 
-// Partial logits: block (ks, tile) computes token tile tile / ET x expert
+// Partial logits: block (tile, ks) computes token tile tile / ET x expert
 // tile tile % ET over the K steps s = ks (mod kLogitSlices).
+// kLo (the pre-normalised block): the router matrix comes as two bf16 parts
+// wr + wr_lo (together exactly W_r * g, the norm gain folded into the router),
+// both multiplied into the same accumulator, and each token's sums are scaled
+// by its 1/rms, row_scale[t].
+template <bool kLo>
 __global__ __launch_bounds__(64) void decode_logits_kernel(const uint16_t* __restrict__ h,
-                                                           const uint16_t* __restrict__ wr, int T, int E, int H,
+                                                           const uint16_t* __restrict__ wr,
+                                                           const uint16_t* __restrict__ wr_lo,
+                                                           const float* __restrict__ row_scale, int T, int E, int H,
                                                            float* __restrict__ part) {
+    constexpr int kSteps = kLo ? kLogitSteps / 2 : kLogitSteps;  // loads per batch: same registers
     const int lane = threadIdx.x;
     const int ET = (E + 15) / 16;
-    const int ks = blockIdx.x, tt = blockIdx.y / ET, et = blockIdx.y - (blockIdx.y / ET) * ET;
+    const int ks = blockIdx.y, tt = blockIdx.x / ET, et = blockIdx.x - (blockIdx.x / ET) * ET;
     const int r = lane & 15, koff = (lane >> 4) * 8;
     const uint16_t* hrow = h + (size_t)min(tt * 16 + r, T - 1) * H;
-    const uint16_t* wrow = wr + (size_t)min(et * 16 + r, E - 1) * H;
+    const size_t woff = (size_t)min(et * 16 + r, E - 1) * H;
     const int nsteps = H / 32;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s0 = ks; s0 < nsteps; s0 += kLogitSlices * kLogitSteps) {
-        bf16x8 av[kLogitSteps], bv[kLogitSteps];
+    for (int s0 = ks; s0 < nsteps; s0 += kLogitSlices * kSteps) {
+        bf16x8 av[kSteps], bv[kSteps], cv[kLo ? kSteps : 1];
 #pragma unroll
-        for (int q = 0; q < kLogitSteps; ++q) {
+        for (int q = 0; q < kSteps; ++q) {
             const int s = s0 + q * kLogitSlices;
             const int kk = (s < nsteps ? s : ks) * 32 + koff;  // past the end: a valid step, discarded
             av[q] = *reinterpret_cast<const bf16x8*>(hrow + kk);
-            bv[q] = *reinterpret_cast<const bf16x8*>(wrow + kk);
+            bv[q] = *reinterpret_cast<const bf16x8*>(wr + woff + kk);
+            if constexpr (kLo) cv[q] = *reinterpret_cast<const bf16x8*>(wr_lo + woff + kk);
         }
         __builtin_amdgcn_sched_barrier(0);  // the whole batch of loads ahead of the MFMAs
 #pragma unroll
-        for (int q = 0; q < kLogitSteps; ++q)
-            if (s0 + q * kLogitSlices < nsteps) acc = mfma16(av[q], bv[q], acc);
+        for (int q = 0; q < kSteps; ++q)
+            if (s0 + q * kLogitSlices < nsteps) {
+                acc = mfma16(av[q], bv[q], acc);
+                if constexpr (kLo) acc = mfma16(av[q], cv[q], acc);
+            }
     }
     // D[j]: token 4(l/16)+j of the token tile, expert l%16 of the expert tile
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int t = tt * 16 + (lane >> 4) * 4 + j, e = et * 16 + r;
-        if (t < T && e < E) part[((size_t)ks * T + t) * E + e] = acc[j];
+        if (t < T && e < E) {
+            float v = acc[j];
+            if constexpr (kLo) v *= row_scale[t];
+            part[((size_t)ks * T + t) * E + e] = v;
+        }
     }
 }
 
@@ -794,11 +810,17 @@ bool decode_fused(int act_dtype, int T, int H, int I, int E, int k) {
 
 size_t decode_logit_part_bytes(int T, int E) { return (size_t)kLogitSlices * T * E * 4; }
 
-hipError_t launch_decode_logits(const void* h, const void* w_router, int T, int H, int E, float* part,
-                                hipStream_t stream) {
-    const dim3 grid(kLogitSlices, ((T + 15) / 16) * ((E + 15) / 16));
-    decode_logits_kernel<<<grid, 64, 0, stream>>>(reinterpret_cast<const uint16_t*>(h),
-                                                  reinterpret_cast<const uint16_t*>(w_router), T, E, H, part);
+hipError_t launch_decode_logits(const void* h, const void* w_router, const void* w_router_lo,
+                                const float* row_scale, int T, int H, int E, float* part, hipStream_t stream) {
+    const dim3 grid(((T + 15) / 16) * ((E + 15) / 16), kLogitSlices);
+    if (w_router_lo)
+        decode_logits_kernel<true><<<grid, 64, 0, stream>>>(
+            reinterpret_cast<const uint16_t*>(h), reinterpret_cast<const uint16_t*>(w_router),
+            reinterpret_cast<const uint16_t*>(w_router_lo), row_scale, T, E, H, part);
+    else
+        decode_logits_kernel<false><<<grid, 64, 0, stream>>>(reinterpret_cast<const uint16_t*>(h),
+                                                             reinterpret_cast<const uint16_t*>(w_router), nullptr,
+                                                             nullptr, T, E, H, part);
     return hipGetLastError();
 }
 

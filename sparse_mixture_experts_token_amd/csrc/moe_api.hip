@@ -48,14 +48,15 @@ struct Layout {
 };
 
 // router_dt: the router's input format (-1: the activation format).  The
-// partial-logits kernel and the fused decode routing take bf16 input only.
-Layout layout(const moe_problem* p, int router_dt = -1) {
+// partial-logits kernel and the fused decode routing take bf16 input only;
+// all_plogits: partial logits at every T (the block's folded router).
+Layout layout(const moe_problem* p, int router_dt = -1, bool all_plogits = false) {
     Layout L{};
     const int rdt = router_dt < 0 ? p->act_dtype : router_dt;
     const size_t tk = (size_t)p->T * p->k;
     L.decode = moe::decode_path(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
     L.fused = rdt == MOE_BF16 && moe::decode_fused(p->act_dtype, p->T, p->H, p->I, p->E, p->k);
-    L.plogits = rdt == MOE_BF16 && p->T <= 64;
+    L.plogits = rdt == MOE_BF16 && (p->T <= 64 || all_plogits);
     L.BM = L.decode ? moe::decode_block_m() : moe::gemm_block_m(p->act_dtype, p->expert_dtype, p->T, p->k, p->E);
     L.nblk = (p->T + moe::kRouterTokens - 1) / moe::kRouterTokens;
     L.max_tiles = (int)((tk + L.BM - 1) / L.BM) + p->E;
@@ -84,24 +85,26 @@ Layout layout(const moe_problem* p, int router_dt = -1) {
     return L;
 }
 
-// The block entry point's workspace: the layer's, then the normalised input
-// in fp32 (the router's input; also the GEMMs' for fp32 activations) and, for
-// bf16 activations, in bf16 (the GEMMs' input) and the router widened to fp32.
+// The block entry point's workspace: the layer's, then for bf16 activations
+// the GEMMs' bf16 input, each token's 1/rms and the router with the gain
+// folded in (two bf16 parts); for fp32 activations the fp32 normalised input
+// (the router's and the GEMMs').
 struct BlockLayout {
     Layout L;
-    size_t n32, n16, wr32, br32, total;
+    size_t n32, n16, rs, whi, wlo, total;
 };
 
 BlockLayout block_layout(const moe_problem* p) {
     BlockLayout B{};
-    B.L = layout(p, MOE_F32);
-    const size_t th = (size_t)p->T * p->H;
     const bool bf = p->act_dtype == MOE_BF16;
+    B.L = bf ? layout(p, MOE_BF16, true) : layout(p, MOE_F32);
+    const size_t th = (size_t)p->T * p->H, eh = (size_t)p->E * p->H;
     size_t o = B.L.total;
-    B.n32 = o;  o = align_up(o + th * 4);
-    B.n16 = o;  o = align_up(o + (bf ? th * 2 : 0));
-    B.wr32 = o; o = align_up(o + (bf ? (size_t)p->E * p->H * 4 : 0));
-    B.br32 = o; o = align_up(o + (bf ? (size_t)p->E * 4 : 0));
+    B.n32 = o; o = align_up(o + (bf ? 0 : th * 4));
+    B.n16 = o; o = align_up(o + (bf ? th * 2 : 0));
+    B.rs = o;  o = align_up(o + (bf ? (size_t)p->T * 4 : 0));
+    B.whi = o; o = align_up(o + (bf ? eh * 2 : 0));
+    B.wlo = o; o = align_up(o + (bf ? eh * 2 : 0));
     B.total = o;
     return B;
 }
@@ -162,7 +165,9 @@ struct PassIn {
     int router_dt;         // format of router_h, w_router and b_router
     const void* router_h;  // the router's input [T, H]
     const void* w_router;
-    const void* b_router;  // may be null
+    const void* w_router_lo;  // bf16 router as two parts (partial logits only), or null
+    const float* row_scale;   // per-token scale of the partial logits, or null
+    const void* b_router;     // may be null
     const void* gemm_h;    // the expert GEMMs' input [T, H] (act dtype)
     const void* residual;  // added in the combine (act dtype) or null
     // pre-norm prologue (norm_g null: none), writing n32 / n16 / wr32 / br32
@@ -171,8 +176,9 @@ struct PassIn {
     const void* x;
     float* n32;
     uint16_t* n16;
-    float* wr32;
-    float* br32;
+    float* rs;
+    uint16_t* whi;
+    uint16_t* wlo;
 };
 
 int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void* out, const moe_routing* routing,
@@ -203,12 +209,13 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     float* part = (float*)(ws + L.part);
     mark(0);
     if (in.norm_g) {
-        e = moe::launch_rms_norm(p->act_dtype, in.x, in.norm_g, in.eps, p->T, p->H, in.n32, in.n16, w->w_router,
-                                 w->b_router, p->E, in.wr32, in.br32, stream);
+        e = moe::launch_rms_norm(p->act_dtype, in.x, in.norm_g, in.eps, p->T, p->H, in.n32, in.n16, in.rs,
+                                 w->w_router, p->E, in.whi, in.wlo, stream);
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
     if (L.plogits) {
-        e = moe::launch_decode_logits(in.router_h, in.w_router, p->T, p->H, p->E, part, stream);
+        e = moe::launch_decode_logits(in.router_h, in.w_router, in.w_router_lo, in.row_scale, p->T, p->H, p->E,
+                                      part, stream);
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
     if (!L.fused) {
@@ -328,16 +335,28 @@ int moe_block_forward(const moe_problem* p, const moe_weights* w, const void* no
     in.norm_g = norm_weight;
     in.eps = eps;
     in.x = x;
-    in.n32 = (float*)(ws + B.n32);
-    in.n16 = bf ? (uint16_t*)(ws + B.n16) : nullptr;
-    in.wr32 = bf ? (float*)(ws + B.wr32) : nullptr;
-    in.br32 = bf ? (float*)(ws + B.br32) : nullptr;
-    in.router_dt = MOE_F32;  // logits from the fp32 normalised input
-    in.router_h = in.n32;
-    in.w_router = bf ? (const void*)in.wr32 : w->w_router;
-    in.b_router = bf ? (w->b_router ? (const void*)in.br32 : nullptr) : w->b_router;
-    in.gemm_h = bf ? (const void*)in.n16 : (const void*)in.n32;
     in.residual = x;
+    in.b_router = w->b_router;
+    if (bf) {
+        // logits r_t * (x . (W_r * g)) from x itself and the folded router
+        in.n16 = (uint16_t*)(ws + B.n16);
+        in.rs = (float*)(ws + B.rs);
+        in.whi = (uint16_t*)(ws + B.whi);
+        in.wlo = (uint16_t*)(ws + B.wlo);
+        in.router_dt = MOE_BF16;
+        in.router_h = x;
+        in.w_router = in.whi;
+        in.w_router_lo = in.wlo;
+        in.row_scale = in.rs;
+        in.gemm_h = in.n16;
+    } else {
+        // the fp32 router on the fp32 normalised input
+        in.n32 = (float*)(ws + B.n32);
+        in.router_dt = MOE_F32;
+        in.router_h = in.n32;
+        in.w_router = w->w_router;
+        in.gemm_h = in.n32;
+    }
     return run_pass(p, w, in, out, routing, ws, B.L, reinterpret_cast<hipStream_t>(stream_v));
 }
 

@@ -285,8 +285,11 @@ struct FusedRouting {
 };
 bool decode_fused(int act_dtype, int T, int H, int I, int E, int k);
 size_t decode_logit_part_bytes(int T, int E);
-hipError_t launch_decode_logits(const void* h, const void* w_router, int T, int H, int E, float* part,
-                                hipStream_t stream);
+// With w_router_lo non-null (the pre-normalised block) the router is the sum
+// of two bf16 matrices w_router + w_router_lo and every token's sums are
+// scaled by row_scale[t].
+hipError_t launch_decode_logits(const void* h, const void* w_router, const void* w_router_lo,
+                                const float* row_scale, int T, int H, int E, float* part, hipStream_t stream);
 hipError_t launch_route_gateup_decode(const GemmProblem& p, const FusedRouting& r, hipStream_t stream);
 int mxfp4_max_k();                   // largest H or I the MXFP4 kernels take
 hipError_t launch_gateup(const GemmProblem& p, hipStream_t stream);
@@ -297,11 +300,12 @@ hipError_t launch_down(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k, const void* residual,
                           hipStream_t stream);
 
-// Block prologue: n32 = g * x / sqrt(mean(x^2) + eps) in fp32 [T, H], and for
-// bf16 activations n16 = n32 rounded to bf16 plus the router widened to fp32
-// (wr32 [E, H], br32 [E] when b_router is not null).
+// Block prologue, r_t = 1 / sqrt(mean(x[t]^2) + eps) in fp32.  bf16
+// activations: row_scale[t] = r_t, n16 = bf16(g * x * r_t) [T, H], and the
+// router with the gain folded in, split exactly into two bf16 parts
+// wr_hi + wr_lo = W_r * g [E, H].  fp32 activations: n32 = g * x * r_t.
 hipError_t launch_rms_norm(int act_dtype, const void* x, const void* g, float eps, int T, int H, float* n32,
-                           uint16_t* n16, const void* w_router, const void* b_router, int E, float* wr32,
-                           float* br32, hipStream_t stream);
+                           uint16_t* n16, float* row_scale, const void* w_router, int E, uint16_t* wr_hi,
+                           uint16_t* wr_lo, hipStream_t stream);
 
 }  // namespace moe

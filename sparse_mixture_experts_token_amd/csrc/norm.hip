@@ -8,21 +8,23 @@
 // One wave per token.  The mean square is accumulated in fp32: each lane sums
 // its 16-byte chunks in order, then the lanes are added by the fixed DPP
 // reduction, so the result does not depend on scheduling.  A second pass over
-// the row (now in L1/L2) writes
-//   n32 = (g * x) * r_t in fp32 - the router's input: for bf16 x and g the
-//         product g * x is exact in fp32, so the logits see the normalised
-//         input to fp32 precision;
-//   n16 = n32 rounded to bf16 (bf16 activations only) - the expert GEMMs'
-//         input, in the format they multiply in.
-// With bf16 activations the router then runs in fp32: blocks past the tokens
-// widen W_r and b_r to fp32 (exact).
+// the row (now in L1/L2) writes the expert GEMMs' input, in the format they
+// multiply in:
+//   bf16 activations: n16 = (g * x) * r_t rounded once to bf16;
+//   fp32 activations: n32 = (g * x) * r_t, also the fp32 router's input.
+// bf16 routing must not see the rounded n16 (a last-bit difference would move
+// a logit by ~1e-4): the logits are r_t * (x . (W_r * g)), x taken exactly.
+// Blocks past the tokens fold the gain into the router: W_r * g, a product of
+// two bf16 values, has at most 16 significant bits, so it splits exactly into
+// hi = bf16(W_r * g) and lo = W_r * g - hi (at most 8 bits: a bf16 value),
+// which the bf16 logit kernel multiplies by x in two MFMAs.
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
 constexpr int kNormWaves = 4;  // tokens per workgroup
-constexpr int kWidenPerBlock = 256 * 8;
+constexpr int kFoldPerBlock = 256 * 8;
 
 template <bool kBf16>
 struct Chunk;  // one 16-byte load: 8 bf16 or 4 fp32 values
@@ -56,21 +58,24 @@ __global__ __launch_bounds__(kNormWaves * 64) void rms_norm_kernel(const void* _
                                                                     const void* __restrict__ g, float eps, int T,
                                                                     int H, float* __restrict__ n32,
                                                                     uint16_t* __restrict__ n16,
-                                                                    const uint16_t* __restrict__ w_router,
-                                                                    const uint16_t* __restrict__ b_router, int E,
-                                                                    float* __restrict__ wr32,
-                                                                    float* __restrict__ br32) {
+                                                                    float* __restrict__ row_scale,
+                                                                    const uint16_t* __restrict__ w_router, int E,
+                                                                    uint16_t* __restrict__ wr_hi,
+                                                                    uint16_t* __restrict__ wr_lo) {
     using C = Chunk<kBf16>;
     constexpr int N = C::N;
     const int tblocks = (T + kNormWaves - 1) / kNormWaves;
     if ((int)blockIdx.x >= tblocks) {
-        // widen the router to fp32 (bf16 activations only)
-        const size_t i0 = ((size_t)blockIdx.x - tblocks) * kWidenPerBlock;
+        // the router with the gain folded in, as two exact bf16 parts (bf16 only)
+        const uint16_t* gb = reinterpret_cast<const uint16_t*>(g);
+        const size_t i0 = ((size_t)blockIdx.x - tblocks) * kFoldPerBlock;
         const size_t nw = (size_t)E * H;
-        for (size_t i = i0 + threadIdx.x; i < i0 + kWidenPerBlock && i < nw; i += blockDim.x)
-            wr32[i] = bf16_bits_to_f32(w_router[i]);
-        if (blockIdx.x == (unsigned)tblocks && b_router)
-            for (int e = threadIdx.x; e < E; e += blockDim.x) br32[e] = bf16_bits_to_f32(b_router[e]);
+        for (size_t i = i0 + threadIdx.x; i < i0 + kFoldPerBlock && i < nw; i += blockDim.x) {
+            const float p = bf16_bits_to_f32(w_router[i]) * bf16_bits_to_f32(gb[i % (size_t)H]);
+            const uint32_t hi = f32_to_bf16_bits(p);
+            wr_hi[i] = (uint16_t)hi;
+            wr_lo[i] = (uint16_t)f32_to_bf16_bits(p - bf16_bits_to_f32(hi));
+        }
         return;
     }
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -87,6 +92,8 @@ __global__ __launch_bounds__(kNormWaves * 64) void rms_norm_kernel(const void* _
     }
     ss = wave_sum(ss);
     const float r = 1.0f / sqrtf(ss / (float)H + eps);
+    if constexpr (kBf16)
+        if (lane == 0) row_scale[t] = r;
     for (int c = lane; c < nc; c += 64) {
         float v[N], gv[N];
         C::load(x, row + c, v);
@@ -94,10 +101,9 @@ __global__ __launch_bounds__(kNormWaves * 64) void rms_norm_kernel(const void* _
         float o[N];
 #pragma unroll
         for (int j = 0; j < N; ++j) o[j] = (gv[j] * v[j]) * r;
-        float4* d = reinterpret_cast<float4*>(n32 + (row + c) * N);
-#pragma unroll
-        for (int j = 0; j < N / 4; ++j) d[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
-        if constexpr (kBf16) {
+        if constexpr (!kBf16) {
+            reinterpret_cast<float4*>(n32)[row + c] = make_float4(o[0], o[1], o[2], o[3]);
+        } else {
             uint4 q;
             q.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
             q.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
@@ -111,13 +117,13 @@ __global__ __launch_bounds__(kNormWaves * 64) void rms_norm_kernel(const void* _
 }  // namespace
 
 hipError_t launch_rms_norm(int act_dtype, const void* x, const void* g, float eps, int T, int H, float* n32,
-                           uint16_t* n16, const void* w_router, const void* b_router, int E, float* wr32,
-                           float* br32, hipStream_t stream) {
+                           uint16_t* n16, float* row_scale, const void* w_router, int E, uint16_t* wr_hi,
+                           uint16_t* wr_lo, hipStream_t stream) {
     const int tblocks = (T + kNormWaves - 1) / kNormWaves;
     if (act_dtype == DT_BF16) {
-        const int wblocks = (int)(((size_t)E * H + kWidenPerBlock - 1) / kWidenPerBlock);
+        const int wblocks = (int)(((size_t)E * H + kFoldPerBlock - 1) / kFoldPerBlock);
         rms_norm_kernel<true><<<tblocks + wblocks, kNormWaves * 64, 0, stream>>>(
-            x, g, eps, T, H, n32, n16, (const uint16_t*)w_router, (const uint16_t*)b_router, E, wr32, br32);
+            x, g, eps, T, H, nullptr, n16, row_scale, (const uint16_t*)w_router, E, wr_hi, wr_lo);
     } else {
         rms_norm_kernel<false><<<tblocks, kNormWaves * 64, 0, stream>>>(x, g, eps, T, H, n32, nullptr, nullptr,
                                                                        nullptr, E, nullptr, nullptr);
