@@ -25,7 +25,9 @@ Sources (web pages; cited by title and section):
   output is added back to the residual stream.
 * "openai/gpt-oss-20b" fixture comparison page, Preserved properties and
   Config changes tables: ``hidden_act = silu``; the fixture shape.
-* "gpt-oss-20b and gpt-oss-120b" explainer, "Four-bit expert weights": MXFP4
+* "gpt-oss-20b and gpt-oss-120b" explainer, "Two attention savings, and a
+  sink": the learned per-head sink in the attention normalisation and its
+  worked example.  "Four-bit expert weights": MXFP4
   groups share a scale, 4.25 bits per parameter, decoded exactly.  The element
   and scale encodings (E2M1, E8M0, 32-element groups) are those of the OCP
   Microscaling Formats (MX) v1.0 specification.
@@ -48,6 +50,7 @@ from .moe import (
     LayerWeights,
 )
 from .block import rms_norm, block_forward, block_forward_per_token
+from .attention import sink_softmax, attn_sink_decode
 
 __all__ = [
     "e2m1_value", "e8m0_value", "mxfp4_dequant", "mxfp4_bits_per_param",
@@ -55,4 +58,5 @@ __all__ = [
     "silu", "swiglu_expert", "moe_forward", "moe_forward_per_token",
     "routing_metadata", "expand_silent", "LayerWeights",
     "rms_norm", "block_forward", "block_forward_per_token",
+    "sink_softmax", "attn_sink_decode",
 ]

@@ -497,3 +497,81 @@ def test_block_two_evaluations_agree():
         a = oracle.block_forward(h, g, 1e-5, w, k)["out"]
         b = oracle.block_forward_per_token(h, g, 1e-5, w, k)
         np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-14)
+
+
+# --------------------------------------------------- attention with sinks --
+
+def _golden_sink():
+    rows = [l.split() for l in open(os.path.join(GOLD, "attention_sink_example.txt")) if l.strip() and l[0] != "#"]
+    d = {r[0]: [float(x) for x in r[1:]] for r in rows}
+    return np.array(d["values"]), d["no_sink"][0], d["sink_equal_score"][0]
+
+
+def test_sink_worked_example_from_the_page():
+    vals, no_sink, with_sink = _golden_sink()
+    s = np.full(3, 0.7)
+    assert oracle.sink_softmax(s, -np.inf) @ vals == pytest.approx(no_sink, rel=1e-15)
+    assert oracle.sink_softmax(s, 0.7) @ vals == pytest.approx(with_sink, rel=1e-15)
+    # the same example through the decode attention: one head, D = 1, q = 1, k = 0 (equal scores)
+    q = np.ones((1, 1, 1))
+    k = np.zeros((1, 1, 3, 1))
+    v = vals.reshape(1, 1, 3, 1)
+    out = oracle.attn_sink_decode(q, k, v, np.array([0.0]), np.array([3]), 0, 1.0)
+    assert out[0, 0, 0] == pytest.approx(with_sink, rel=1e-15)
+
+
+def test_sink_to_minus_infinity_is_plain_softmax():
+    from scipy.special import softmax
+    s = np.random.default_rng(60).standard_normal((4, 9)) * 3
+    np.testing.assert_allclose(oracle.sink_softmax(s, -np.inf), softmax(s, axis=-1), rtol=1e-14)
+
+
+def test_sink_weight_fills_the_gap_to_one():
+    """Real-token weights sum to 1 - exp(sink) / (exp(sink) + sum exp(s))."""
+    rng = np.random.default_rng(61)
+    s, sink = rng.standard_normal(7), 0.3
+    w = oracle.sink_softmax(s, sink)
+    assert w.sum() == pytest.approx(1 - np.exp(sink) / (np.exp(sink) + np.exp(s).sum()), rel=1e-14)
+    assert np.all(w > 0) and w.sum() < 1
+    # a dominant sink silences the head
+    assert np.abs(oracle.sink_softmax(s, 800.0)).max() < 1e-300
+
+
+def test_attention_one_key_window_closed_form():
+    """Window 1: only the newest key, out = v_last * e^s / (e^s + e^sink)."""
+    rng = np.random.default_rng(62)
+    B, Hq, Hkv, Tk, D = 2, 4, 2, 5, 8
+    q, k, v = rng.standard_normal((B, Hq, D)), rng.standard_normal((B, Hkv, Tk, D)), rng.standard_normal((B, Hkv, Tk, D))
+    sinks, lens = rng.standard_normal(Hq), np.array([5, 3])
+    out = oracle.attn_sink_decode(q, k, v, sinks, lens, 1, 0.25)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // 2
+            s = 0.25 * q[b, h] @ k[b, g, lens[b] - 1]
+            w = np.exp(s) / (np.exp(s) + np.exp(sinks[h]))
+            np.testing.assert_allclose(out[b, h], w * v[b, g, lens[b] - 1], rtol=1e-13)
+
+
+def test_attention_head_groups_and_window_by_brute_force():
+    """Against an explicit double loop over heads and keys (window and lengths
+    applied by position tests), and a permutation of the query heads inside a
+    group permutes the output the same way."""
+    rng = np.random.default_rng(63)
+    B, Hq, Hkv, Tk, D = 3, 8, 2, 40, 4
+    q, k, v = rng.standard_normal((B, Hq, D)), rng.standard_normal((B, Hkv, Tk, D)), rng.standard_normal((B, Hkv, Tk, D))
+    sinks, lens = rng.standard_normal(Hq), np.array([40, 17, 1])
+    for window in (0, 6):
+        out = oracle.attn_sink_decode(q, k, v, sinks, lens, window, 0.5)
+        for b in range(B):
+            for h in range(Hq):
+                num, den = np.zeros(D), np.exp(sinks[h])
+                for j in range(Tk):
+                    if j >= lens[b] or (window and j < lens[b] - window):
+                        continue
+                    e = np.exp(0.5 * sum(q[b, h, d] * k[b, h // 4, j, d] for d in range(D)))
+                    num += e * v[b, h // 4, j]
+                    den += e
+                np.testing.assert_allclose(out[b, h], num / den, rtol=1e-12)
+    perm = np.array([1, 0, 3, 2, 4, 5, 7, 6])
+    a = oracle.attn_sink_decode(q[:, perm], k, v, sinks[perm], lens, 0, 0.5)
+    np.testing.assert_allclose(a, oracle.attn_sink_decode(q, k, v, sinks, lens, 0, 0.5)[:, perm], rtol=1e-14)
