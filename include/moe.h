@@ -165,6 +165,37 @@ int moe_block_forward(const moe_problem *p, const moe_weights *w, const void *no
                       const void *x, void *out, const moe_routing *routing, void *workspace,
                       size_t workspace_bytes, void *stream);
 
+/* Decode attention with learned sinks ("gpt-oss-20b and gpt-oss-120b"
+ * explainer, "Two attention savings, and a sink"; "gpt-oss 20B" field guide,
+ * cutaway 05): the newest token of each of B sequences attends to its
+ * key/value cache.  For query head h (key/value head g = h / (Hq/Hkv)):
+ *     s_j = scale * q[b,h] . k[b,g,j]
+ *     out[b,h] = sum_j exp(s_j) v[b,g,j] / (exp(sinks[h]) + sum_j exp(s_j))
+ * over the visible keys j: 0 <= j < len_b, and with window > 0 only the last
+ * `window` of them (len_b - window <= j, the newest key included).  The sink
+ * joins the normalisation and contributes no value.
+ * Layouts (bf16, row-major, 16-byte aligned): q [B, Hq, D], k_cache and
+ * v_cache [B, Hkv, Tk, D], out [B, Hq, D]; sinks [Hq] bf16; lens [B] int32
+ * device array (NULL: every sequence has Tk keys; values are clamped to
+ * 0..Tk, and a sequence with no visible keys gives 0).  Scores, softmax and
+ * sums in fp32, out rounded once.  Supported: Hq a multiple of Hkv with
+ * Hq/Hkv <= 8, D a multiple of 8 up to 64, Tk >= 1, window >= 0, B >= 0
+ * (B = 0 is a no-op).  The keys of a sequence are split over workgroups;
+ * `workspace` (16-byte aligned, moe_attn_workspace_bytes(p) bytes, caller
+ * owned, not to be touched until the stream has passed this call) holds the
+ * partial results.  moe_attn_workspace_bytes returns 0 for invalid sizes.
+ * Errors: MOE_ERR_NULL (p, q, k_cache, v_cache, sinks, out or workspace NULL
+ * while B > 0), MOE_ERR_SHAPE (unsupported sizes, scale not finite),
+ * MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP. */
+typedef struct {
+    int32_t B, Hq, Hkv, Tk, D, window;
+    float scale;
+} moe_attn_problem;
+size_t moe_attn_workspace_bytes(const moe_attn_problem *p);
+int moe_attn_sink_decode(const moe_attn_problem *p, const void *q, const void *k_cache, const void *v_cache,
+                         const void *sinks, const int32_t *lens, void *out, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* Silent expansion ("gpt-oss-40b-64a8-init" page, section 2 Principle/Proof,
  * section 5.2): for every per-expert tensor of *src (w_router, b_router,
  * w_gate, w_up, w_down and, for MXFP4, the three scale tensors) write

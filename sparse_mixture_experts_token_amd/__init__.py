@@ -12,6 +12,8 @@ The functions mirror the C entry points of ``include/moe.h``:
 * ``moe_forward(problem, weights, h, out, routing=None, workspace=None)``
 * ``moe_block_workspace_bytes(problem)``
 * ``moe_block_forward(problem, weights, norm_weight, eps, x, out, routing=None, workspace=None)``
+* ``moe_attn_workspace_bytes(problem)``
+* ``moe_attn_sink_decode(problem, q, k_cache, v_cache, sinks, lens, out, workspace=None)``
 * ``moe_expand_silent(base, src, M, dst)``
 * ``moe_status_string(status)``
 * ``moe_profile_begin(max_calls)`` / ``moe_profile_begin_mask(max_calls, mask)`` / ``moe_profile_end()``
@@ -37,7 +39,7 @@ MOE_NUM_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_HIP", -7: "MOE_ERR_STATE"}
 EXPORTED = ("moe_workspace_bytes", "moe_forward", "moe_block_workspace_bytes", "moe_block_forward",
-            "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
+            "moe_attn_workspace_bytes", "moe_attn_sink_decode", "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
             "moe_profile_begin", "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name")
 MOE_PROFILE_ALL = (1 << (MOE_NUM_STAGES + 1)) - 1
 
@@ -55,6 +57,27 @@ class _Problem(ctypes.Structure):
 
 _WEIGHT_FIELDS = ("w_router", "b_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
 _ROUTING_FIELDS = ("logits", "topk_idx", "topk_w", "expert_offsets", "perm_src")
+
+
+class _AttnProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("Tk", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("window", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+@dataclass
+class AttnProblem:
+    """Sizes of decode attention with sinks (``moe_attn_problem``)."""
+    B: int
+    Hq: int
+    Hkv: int
+    Tk: int
+    D: int
+    window: int = 0
+    scale: float = 0.0  # 0: 1/sqrt(D)
+
+    def _c(self) -> _AttnProblem:
+        sc = self.scale if self.scale else 1.0 / float(self.D) ** 0.5
+        return _AttnProblem(self.B, self.Hq, self.Hkv, self.Tk, self.D, self.window, sc)
 
 
 class _Weights(ctypes.Structure):
@@ -102,6 +125,11 @@ def load() -> ctypes.CDLL:
                                       ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.moe_block_forward.restype = ctypes.c_int
+    lib.moe_attn_workspace_bytes.argtypes = [ctypes.POINTER(_AttnProblem)]
+    lib.moe_attn_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_attn_sink_decode.argtypes = [ctypes.POINTER(_AttnProblem)] + [ctypes.c_void_p] * 7 + [
+        ctypes.c_size_t, ctypes.c_void_p]
+    lib.moe_attn_sink_decode.restype = ctypes.c_int
     lib.moe_expand_silent.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_int32,
                                       ctypes.POINTER(_Weights), ctypes.c_void_p]
     lib.moe_expand_silent.restype = ctypes.c_int
@@ -218,6 +246,23 @@ def moe_block_forward(problem: Problem, weights: dict, norm_weight, eps: float, 
                                ctypes.byref(r) if r is not None else None, _ptr(workspace), int(workspace_bytes),
                                _stream(stream))
     _check(st)
+
+
+def moe_attn_workspace_bytes(problem: AttnProblem) -> int:
+    p = problem._c()
+    return int(load().moe_attn_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_attn_sink_decode(problem: AttnProblem, q, k_cache, v_cache, sinks, lens, out, workspace=None,
+                         workspace_bytes: int | None = None, stream=None) -> None:
+    """Enqueue decode attention with sinks on ``stream`` (default: torch's
+    current stream); ``lens`` may be None (every sequence has Tk keys);
+    ``workspace`` defaults to a fresh torch allocation of the required size."""
+    lib = load()
+    p = problem._c()
+    workspace, workspace_bytes = _workspace(lib.moe_attn_workspace_bytes, p, q, workspace, workspace_bytes)
+    _check(lib.moe_attn_sink_decode(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(sinks),
+                                    _ptr(lens), _ptr(out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def moe_expand_silent(base: Problem, src: dict, M: int, dst: dict, stream=None) -> None:

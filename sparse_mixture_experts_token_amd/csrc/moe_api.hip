@@ -360,6 +360,30 @@ int moe_block_forward(const moe_problem* p, const moe_weights* w, const void* no
     return run_pass(p, w, in, out, routing, ws, B.L, reinterpret_cast<hipStream_t>(stream_v));
 }
 
+size_t moe_attn_workspace_bytes(const moe_attn_problem* p) {
+    if (!p || !moe::attn_sink_shape_ok(p->B, p->Hq, p->Hkv, p->Tk, p->D, p->window)) return 0;
+    return moe::attn_workspace_bytes(p->B, p->Hq, p->Hkv, p->Tk, p->D, p->window);
+}
+
+int moe_attn_sink_decode(const moe_attn_problem* p, const void* q, const void* k_cache, const void* v_cache,
+                         const void* sinks, const int32_t* lens, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream_v) {
+    if (!p) return MOE_ERR_NULL;
+    if (!moe::attn_sink_shape_ok(p->B, p->Hq, p->Hkv, p->Tk, p->D, p->window)) return MOE_ERR_SHAPE;
+    if (!(p->scale == p->scale) || p->scale > 3.0e38f || p->scale < -3.0e38f) return MOE_ERR_SHAPE;
+    if (p->B == 0) return MOE_OK;
+    if (!q || !k_cache || !v_cache || !sinks || !out || !workspace) return MOE_ERR_NULL;
+    for (const void* t : {q, k_cache, v_cache, (const void*)out, (const void*)workspace})
+        if (!aligned(t, 16)) return MOE_ERR_ALIGN;
+    if (!aligned(sinks, 2) || (lens && !aligned(lens, 4))) return MOE_ERR_ALIGN;
+    if (workspace_bytes < moe::attn_workspace_bytes(p->B, p->Hq, p->Hkv, p->Tk, p->D, p->window))
+        return MOE_ERR_WORKSPACE;
+    const hipError_t e = moe::launch_attn_sink_decode(q, k_cache, v_cache, sinks, lens, out, workspace, p->B, p->Hq,
+                                                      p->Hkv, p->Tk, p->D, p->window, p->scale,
+                                                      reinterpret_cast<hipStream_t>(stream_v));
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 int moe_expand_silent(const moe_problem* base, const moe_weights* src, int32_t M, const moe_weights* dst,
                       void* stream_v) {
     if (!base || !src || !dst) return MOE_ERR_NULL;

@@ -300,6 +300,17 @@ hipError_t launch_down(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k, const void* residual,
                           hipStream_t stream);
 
+// Decode attention with learned sinks (attn_sink.hip).  Shapes: Hq a multiple
+// of Hkv with at most 8 query heads per key/value head, D a multiple of 8 up
+// to 64, Tk >= 1, window >= 0 (0: all keys).
+// The keys are split into chunks over workgroups; the workspace holds each
+// chunk's partial state (attn_workspace_bytes).
+bool attn_sink_shape_ok(int B, int Hq, int Hkv, int Tk, int D, int window);
+size_t attn_workspace_bytes(int B, int Hq, int Hkv, int Tk, int D, int window);
+hipError_t launch_attn_sink_decode(const void* q, const void* k, const void* v, const void* sinks,
+                                   const int32_t* lens, void* out, void* workspace, int B, int Hq, int Hkv, int Tk,
+                                   int D, int window, float scale, hipStream_t stream);
+
 // Block prologue, r_t = 1 / sqrt(mean(x[t]^2) + eps) in fp32.  bf16
 // activations: row_scale[t] = r_t, n16 = bf16(g * x * r_t) [T, H], and the
 // router with the gain folded in, split exactly into two bf16 parts

@@ -36,7 +36,7 @@ import numpy as np
 ROOT_SEED = 20261203
 
 # tensor ids of the per-tensor streams
-TID_H, TID_WR, TID_BR, TID_GATE, TID_UP, TID_DOWN, TID_HOT, TID_ROWSCALE, TID_NORM = range(9)
+TID_H, TID_WR, TID_BR, TID_GATE, TID_UP, TID_DOWN, TID_HOT, TID_ROWSCALE, TID_NORM, TID_ATTN = range(10)
 
 
 @dataclass(frozen=True)
@@ -241,6 +241,25 @@ def block_inputs(layer: Layer) -> tuple[np.ndarray, np.ndarray]:
         h32 = np.asarray(layer.h, dtype=np.float32)
     g32 = rng_for(c.cid, TID_NORM).uniform(0.5, 1.5, c.H).astype(np.float32)
     return _store(h32 * scale[:, None], c.act), _store(g32, c.act)
+
+
+def attn_inputs(seed: int, B: int, Hq: int, Hkv: int, Tk: int, D: int) -> dict:
+    """Seeded decode-attention inputs in bf16 bits: q [B, Hq, D], k and v
+    [B, Hkv, Tk, D] with N(0, 1) entries, sinks [Hq] ~ N(0, 1), and per-sequence
+    lengths [B] (int32) drawn uniformly from 1..Tk, the first sequence full and,
+    for B > 2, the second of length 1."""
+    r = rng_for(seed, TID_ATTN)
+    out = {"q": f32_to_bf16_bits(r.standard_normal((B, Hq, D), dtype=np.float32)),
+           "k": f32_to_bf16_bits(r.standard_normal((B, Hkv, Tk, D), dtype=np.float32)),
+           "v": f32_to_bf16_bits(r.standard_normal((B, Hkv, Tk, D), dtype=np.float32)),
+           "sinks": f32_to_bf16_bits(r.standard_normal(Hq, dtype=np.float32))}
+    lens = r.integers(1, Tk + 1, size=B).astype(np.int32)
+    if B > 0:
+        lens[0] = Tk
+    if B > 2:
+        lens[1] = 1
+    out["lens"] = lens
+    return out
 
 
 def decode_T(key: int) -> int:

@@ -20,7 +20,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = smoe.load()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(smoe.EXPORTED) == names
@@ -101,6 +101,33 @@ def test_block_argument_errors_return_before_any_launch():
     # T = 0 is a no-op even with no buffers at all
     assert _block(smoe.Problem(0, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_BF16), g=0, x=0, out=0, ws=0,
                   ws_bytes=0) == 0
+
+
+def test_attention_argument_errors_return_before_any_launch():
+    lib = smoe.load()
+
+    def call(P, q=0x1000, k=0x2000, v=0x3000, s=0x4000, lens=None, out=0x5000, ws=0x7000, ws_bytes=1 << 40):
+        p = P._c()
+        return lib.moe_attn_sink_decode(ctypes.byref(p), q, k, v, s, lens, out, ws, ws_bytes, None)
+
+    P = smoe.AttnProblem(4, 64, 8, 300, 64, 128)
+    assert lib.moe_attn_sink_decode(None, 1, 1, 1, 1, None, 1, 1, 1, None) == -1
+    need = lib.moe_attn_workspace_bytes(ctypes.byref(P._c()))
+    assert need > 0 and lib.moe_attn_workspace_bytes(ctypes.byref(smoe.AttnProblem(4, 60, 8, 300, 64)._c())) == 0
+    assert call(P, ws_bytes=need - 1) == -4
+    assert call(P, ws=0) == -1
+    assert call(P, ws=0x7004) == -5
+    for bad in (dict(Hq=60), dict(Hq=128, Hkv=8), dict(D=12), dict(D=72), dict(Tk=0), dict(window=-1), dict(Hkv=0)):
+        kw = dict(B=4, Hq=64, Hkv=8, Tk=300, D=64, window=0)
+        kw.update(bad)
+        assert call(smoe.AttnProblem(**kw)) == -2, bad
+    assert call(smoe.AttnProblem(4, 64, 8, 300, 64, 0, float("nan"))) == -2
+    assert call(P, q=0) == -1
+    assert call(P, s=0) == -1
+    assert call(P, k=0x2008) == -5
+    assert call(P, lens=0x6002) == -5
+    # B = 0 is a no-op even with no buffers
+    assert call(smoe.AttnProblem(0, 64, 8, 300, 64), q=0, k=0, v=0, s=0, out=0, ws=0, ws_bytes=0) == 0
 
 
 def test_expand_and_decode_argument_errors():
