@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--attn-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -97,6 +98,42 @@ def cpu_baseline(key, T_sample):
     return {"value": T_sample / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {T_sample} of the {c.T} prefill tokens, whole layer in fp64 (NumPy), "
                       f"expert weights generated and widened on the fly; {dt:.1f} s"}
+
+
+def attention_leg(smoe, torch, dev, steps):
+    """Decode attention with sinks at the gpt-oss-20b head shape (64 query
+    heads, 8 key/value heads, head dim 64): 64 sequences of 4096 cached keys,
+    full attention, seeded N(0, 1) bf16 inputs.  HBM roofline on the bytes the
+    step must read and write: every visible key and value row, q, sinks, out."""
+    B, Hq, Hkv, Tk, D = 64, 64, 8, 4096, 64
+    P = smoe.AttnProblem(B, Hq, Hkv, Tk, D, 0)
+    g = torch.Generator(device=dev).manual_seed(20261203)
+    q = torch.randn((B, Hq, D), generator=g, device=dev).bfloat16()
+    kc = torch.randn((B, Hkv, Tk, D), generator=g, device=dev).bfloat16()
+    vc = torch.randn((B, Hkv, Tk, D), generator=g, device=dev).bfloat16()
+    sinks = torch.randn((Hq,), generator=g, device=dev).bfloat16()
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(smoe.moe_attn_workspace_bytes(P), dtype=torch.uint8, device=dev)
+
+    def astep():
+        smoe.moe_attn_sink_decode(P, q, kc, vc, sinks, None, out, workspace=ws)
+
+    for _ in range(10):
+        astep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        astep()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    byts = 2 * B * Hkv * Tk * D * 2 + 2 * B * Hq * D * 2 + Hq * 2
+    gbps = byts / (ms * 1e-3) / 1e9
+    return {"workload": f"decode attention with sinks, {B} sequences x {Tk} keys, {Hq} query / {Hkv} kv heads, "
+                        f"head dim {D}, full, bf16", "ms_per_step": round(ms, 4), "alg_bytes": byts,
+            "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "kernels": "attn_partial_kernel + attn_merge_kernel"}
 
 
 def main():
@@ -208,6 +245,9 @@ def main():
               "hbm_frac": round(Bd / ddt / 1e9 / PEAK_HBM_GBPS, 4),
               "stage_ms_profiled_pass": [round(x / dcalls, 5) for x in dstage]}
 
+    del wsd, outd, hd
+    attention = attention_leg(smoe, torch, dev, args.attn_steps)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(key, args.cpu_sample_tokens)
@@ -222,7 +262,7 @@ def main():
         "layer_tflops": round(F / (ms_step * 1e-3) / 1e12, 2),
         "layer_mfma_frac": round(F / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "stage_ms_profiled_pass": {smoe.moe_stage_name(i): round(x, 5) for i, x in enumerate(stage_avg)},
-        "roofline": roofline, "decode": decode, "cpu_baseline": cpu,
+        "roofline": roofline, "decode": decode, "attention": attention, "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
 

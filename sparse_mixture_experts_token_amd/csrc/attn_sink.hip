@@ -10,22 +10,27 @@
 //
 // Two kernels.  attn_partial_kernel: one workgroup per (sequence, key/value
 // head, chunk of the visible keys), so that short batches still fill the
-// chip; the group's query heads share every key and value load.  The chunk
-// is cut into 64-key tiles dealt round-robin to four waves.  Per tile:
-//   scores - lane (kq, dc) = (l / 8, l % 8) reads 16 bytes (features
-//            8dc..8dc+7) of key 8r + kq in round r, so one load instruction
-//            covers 8 whole 128-byte key rows; the partial dot products are
-//            summed over the 8 lanes of a key by DPP moves;
-//   softmax - lane = key: a running max m and sum l per head (streaming
-//            softmax); the wave's accumulator is rescaled when m grows;
-//   values  - the same (kq, dc) layout reads the value rows and adds
-//            p * v into per-lane sums of 8 features, reduced over kq at the end.
+// chip; the group's G query heads share every key and value load.  The chunk
+// is cut into 64-key tiles dealt round-robin to four waves.  Per tile, all 16
+// loads of a lane are issued first, then:
+//   scores - a 16x16x32 bf16 MFMA per 16 keys and 32 features: the G query
+//            heads are the A rows (padded to 16 with zeros), the key rows
+//            the B columns, read from HBM straight into operand layout;
+//   softmax - running max m and sum l per head (streaming softmax), reduced
+//            over the 16 lanes that hold a head's keys; the weights go to
+//            LDS as [key][head], with the factor that rescales the sums;
+//   values  - lane (kq, dc) = (l / 8, l % 8) holds 16 bytes (features
+//            8dc..8dc+7) of value row 8r + kq, so one load covers 8 whole
+//            128-byte rows; p * v is added into per-lane fp32 sums, reduced
+//            over kq at the end.  (The MFMA would need the value tile
+//            transposed, key-major per feature; on the vector unit it is
+//            about 600 instructions per tile, under the time of its loads.)
 // The four waves are merged and the chunk's (m, l, sum p v) written to the
 // workspace.  attn_merge_kernel: per (sequence, query head), the chunks are
 // combined with the sink as the starting state (m = sink, l = 1, nothing in
-// the sum), so it joins the normalisation and adds no value.  All in fp32,
-// out rounded once.  Memory bound: every visible key and value row is read
-// once.
+// the sum), so it joins the normalisation and adds no value.  Softmax and
+// sums in fp32, out rounded once.  Memory bound: every visible key and value
+// row is read once.
 #include "moe_internal.h"
 
 namespace moe {
@@ -52,20 +57,6 @@ struct AttnArgs {
     float scale;
 };
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    return x;
-}
-
-// Sum over the 8 lanes of a key group (lanes 8i .. 8i+7), result in all 8.
-__device__ __forceinline__ float sum8(float x) {
-    x += dpp_f<kDppXor1>(x);
-    x += dpp_f<kDppXor2>(x);
-    x += dpp_f<kDppHalfMirror>(x);
-    return x;
-}
-
 __device__ __forceinline__ void unpack8(const uint4 w, float (&f)[8]) {
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -82,100 +73,138 @@ __device__ __forceinline__ void visible(const AttnArgs& a, int b, int& lo, int& 
     lo = (a.window > 0 && n > a.window) ? n - a.window : 0;
 }
 
+// G query heads share each key/value head (G <= 8); one instantiation per G.
+template <int G>
 __global__ __launch_bounds__(kAWaves * 64) void attn_partial_kernel(AttnArgs a) {
-    __shared__ float s_q[kAMaxG][kAMaxD];
-    __shared__ float s_s[kAWaves][kAMaxG][kATile];  // this tile's scores, then weights
-    __shared__ float s_m[kAWaves][kAMaxG], s_l[kAWaves][kAMaxG];
-    __shared__ float s_acc[kAWaves][kAMaxG][kAMaxD];
+    __shared__ __align__(16) float s_p[kAWaves][kATile][8];  // this tile's weights, [key][head]
+    __shared__ __align__(16) float s_corr[kAWaves][8];       // this tile's rescale factor per head
+    __shared__ float s_m[kAWaves][G], s_l[kAWaves][G];
+    __shared__ float s_acc[kAWaves][G][kAMaxD];
     const int c = blockIdx.x % a.nchunk;
     const int bg = blockIdx.x / a.nchunk;
     const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
-    const int G = a.Hq / a.Hkv, D = a.D;
+    const int D = a.D;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int kq = lane >> 3, dc = lane & 7;
+    const int col = lane & 15, grp = lane >> 4;  // MFMA column (key) and row group (heads 4grp..4grp+3)
+    const int kq = lane >> 3, dc = lane & 7;     // value layout: key 8r+kq, features 8dc..8dc+7
     const bool dlive = 8 * dc < D;
-    for (int i = threadIdx.x; i < G * D; i += blockDim.x) {
-        const int h = i / D, d = i - (i / D) * D;
-        s_q[h][d] = bf16_bits_to_f32(a.q[((size_t)b * a.Hq + g * G + h) * D + d]) * a.scale;
-    }
-    __syncthreads();
     int lo, n;
     visible(a, b, lo, n);
     const int kb = lo + c * a.chunk;
     const int ke = min(n, kb + a.chunk);
     const size_t kv0 = ((size_t)b * a.Hkv + g) * a.Tk;
 
-    float m[kAMaxG], l[kAMaxG], acc[kAMaxG][8];
+    // Q as the MFMA A operand: row = head (rows G..15 zero), K = features;
+    // K step ks covers features 32ks..32ks+31, lane's 8 at 32ks + 8grp.
+    bf16x8 qa[2];
 #pragma unroll
-    for (int h = 0; h < kAMaxG; ++h) {
-        m[h] = kNegInf;
-        l[h] = 0.0f;
+    for (int ks = 0; ks < 2; ++ks) {
+        const int f = 32 * ks + 8 * grp;
+        qa[ks] = bf16x8{};
+        if (col < G && f < D)
+            qa[ks] = *reinterpret_cast<const bf16x8*>(a.q + ((size_t)b * a.Hq + g * G + col) * D + f);
+    }
+    const bool ks1 = D > 32;  // uniform
+    const int fk0 = 8 * grp < D ? 8 * grp : 0, fk1 = 32 + 8 * grp < D ? 32 + 8 * grp : 0;
+    const bool klive0 = 8 * grp < D, klive1 = 32 + 8 * grp < D;
+    const int fv = 8 * (dlive ? dc : 0);
+
+    float m[4], l[4], acc[G][8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        m[j] = kNegInf;
+        l[j] = 0.0f;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
-    }
+
     for (int t0 = kb + wave * kATile; t0 < ke; t0 += kAWaves * kATile) {  // wave-uniform
-        // scores: 8 keys per round, 8 lanes per key.  Every lane reads inside
-        // the cache (key t0 is visible, feature chunk 0 exists); lanes past the
-        // chunk or the head dimension discard what they read.  (Issuing all of
-        // a tile's loads at once needs ~160 registers, and the lower occupancy
-        // costs more than the overlap gains.)
-#pragma unroll 2
-        for (int r = 0; r < kATile / 8; ++r) {
+        // key rows as the B operand (column = key t0 + 16blk + col) and value
+        // rows in the value layout, all issued before any is used.  Rows past
+        // the chunk read key t0 (visible) and are masked below.
+        bf16x8 kr[4][2];
+        uint4 vr[8];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+            const int j = t0 + 16 * blk + col;
+            const uint16_t* row = a.k + (kv0 + (j < ke ? j : t0)) * D;
+            kr[blk][0] = *reinterpret_cast<const bf16x8*>(row + fk0);
+            kr[blk][1] = ks1 ? *reinterpret_cast<const bf16x8*>(row + fk1) : bf16x8{};
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
             const int j = t0 + 8 * r + kq;
-            const bool valid = j < ke;
-            const uint4 w = *reinterpret_cast<const uint4*>(a.k + (kv0 + (valid ? j : t0)) * D + 8 * (dlive ? dc : 0));
-            float kf[8];
-            unpack8((valid && dlive) ? w : uint4{0u, 0u, 0u, 0u}, kf);
+            vr[r] = *reinterpret_cast<const uint4*>(a.v + (kv0 + (j < ke ? j : t0)) * D + fv);
+        }
+        // scores: D[j] of block blk = q[head 4grp+j] . k[key t0+16blk+col]
+        float s[4][4];
 #pragma unroll
-            for (int h = 0; h < kAMaxG; ++h) {
-                if (h >= G) break;  // uniform
-                float part = 0.0f;
-                if (dlive) {
+        for (int blk = 0; blk < 4; ++blk) {
+            f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+            d = mfma16(qa[0], klive0 ? kr[blk][0] : bf16x8{}, d);
+            if (ks1) d = mfma16(qa[1], klive1 ? kr[blk][1] : bf16x8{}, d);
+            const bool valid = t0 + 16 * blk + col < ke;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) part = fmaf(s_q[h][8 * dc + e], kf[e], part);
-                }
-                part = sum8(part);
-                if (dc == 0) s_s[wave][h][8 * r + kq] = valid ? part : kNegInf;
+            for (int j = 0; j < 4; ++j) s[blk][j] = valid ? d[j] * a.scale : kNegInf;
+        }
+        // streaming softmax per head over the tile's 64 keys (16 lanes x 4 blocks)
+        float corr[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float mx = fmaxf(fmaxf(s[0][j], s[1][j]), fmaxf(s[2][j], s[3][j]));
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+            const float mn = fmaxf(m[j], mx);  // finite: key t0 is in every 16-lane group
+            corr[j] = __expf(m[j] - mn);
+            float sum = 0.0f;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const float p = s[blk][j] == kNegInf ? 0.0f : __expf(s[blk][j] - mn);
+                s[blk][j] = p;
+                sum += p;
             }
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+            l[j] = l[j] * corr[j] + sum;
+            m[j] = mn;
+        }
+        if (lane < 32) {  // heads 0..7; rows 8..15 are padding
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk)
+                *reinterpret_cast<float4*>(&s_p[wave][16 * blk + col][4 * grp]) =
+                    float4{s[blk][0], s[blk][1], s[blk][2], s[blk][3]};
+            if (col == 0) *reinterpret_cast<float4*>(&s_corr[wave][4 * grp]) = float4{corr[0], corr[1], corr[2], corr[3]};
         }
         __builtin_amdgcn_wave_barrier();
-        // softmax: lane = key of the tile
+        // weighted values: acc[h][e] (features 8dc+e, keys kq mod 8) on VALU
+        {
+            const float4 c0 = *reinterpret_cast<const float4*>(&s_corr[wave][0]);
+            const float4 c1 = *reinterpret_cast<const float4*>(&s_corr[wave][4]);
+            const float cr[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-        for (int h = 0; h < kAMaxG; ++h) {
-            if (h >= G) break;
-            const float s = s_s[wave][h][lane];
-            const float mn = fmaxf(m[h], wave_max(s));  // finite: key t0 is visible
-            const float corr = __expf(m[h] - mn);
-            const float p = s == kNegInf ? 0.0f : __expf(s - mn);
-            l[h] = l[h] * corr + wave_sum(p);
-            m[h] = mn;
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[h][e] *= corr;
-            s_s[wave][h][lane] = p;
+                for (int e = 0; e < 8; ++e) acc[h][e] *= cr[h];
         }
-        __builtin_amdgcn_wave_barrier();
-        // values: the same 8-lanes-per-key layout
-#pragma unroll 2
-        for (int r = 0; r < kATile / 8; ++r) {
-            const int j = t0 + 8 * r + kq;
-            const bool valid = j < ke;
-            const uint4 w = *reinterpret_cast<const uint4*>(a.v + (kv0 + (valid ? j : t0)) * D + 8 * (dlive ? dc : 0));
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
             float vf[8];
-            unpack8((valid && dlive) ? w : uint4{0u, 0u, 0u, 0u}, vf);
+            unpack8(dlive ? vr[r] : uint4{0u, 0u, 0u, 0u}, vf);  // invalid keys have p = 0
+            const float4 p0 = *reinterpret_cast<const float4*>(&s_p[wave][8 * r + kq][0]);
+            const float4 p1 = *reinterpret_cast<const float4*>(&s_p[wave][8 * r + kq][4]);
+            const float pr[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
 #pragma unroll
-            for (int h = 0; h < kAMaxG; ++h) {
-                if (h >= G) break;
-                const float p = s_s[wave][h][8 * r + kq];
+            for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
-            }
+                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
         }
-        __builtin_amdgcn_wave_barrier();  // weights read before the next tile's scores
+        __builtin_amdgcn_wave_barrier();  // weights read before the next tile writes them
     }
     // sum the per-lane values over the 8 key lanes kq (lanes dc, dc+8, ..., dc+56)
 #pragma unroll
-    for (int h = 0; h < kAMaxG; ++h) {
-        if (h >= G) break;
+    for (int h = 0; h < G; ++h) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float x = acc[h][e];
@@ -184,13 +213,18 @@ __global__ __launch_bounds__(kAWaves * 64) void attn_partial_kernel(AttnArgs a) 
             x += __shfl_xor(x, 32, 64);
             acc[h][e] = x;
         }
-        if (lane == 0) {
-            s_m[wave][h] = m[h];
-            s_l[wave][h] = l[h];
-        }
         if (kq == 0 && dlive) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * dc + e] = acc[h][e];
+        }
+    }
+    if (lane < 32 && col == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (4 * grp + j < G) {
+                s_m[wave][4 * grp + j] = m[j];
+                s_l[wave][4 * grp + j] = l[j];
+            }
         }
     }
     __syncthreads();
@@ -281,7 +315,17 @@ hipError_t launch_attn_sink_decode(const void* q, const void* k, const void* v, 
     float* pm = reinterpret_cast<float*>(workspace);
     AttnArgs a{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)sinks, lens,
                (uint16_t*)out, pm, pm + rows, pm + 2 * rows, B, Hq, Hkv, Tk, D, window, nc, ch, scale};
-    attn_partial_kernel<<<B * Hkv * nc, kAWaves * 64, 0, stream>>>(a);
+    const dim3 grid(B * Hkv * nc), block(kAWaves * 64);
+    switch (Hq / Hkv) {
+    case 1: attn_partial_kernel<1><<<grid, block, 0, stream>>>(a); break;
+    case 2: attn_partial_kernel<2><<<grid, block, 0, stream>>>(a); break;
+    case 3: attn_partial_kernel<3><<<grid, block, 0, stream>>>(a); break;
+    case 4: attn_partial_kernel<4><<<grid, block, 0, stream>>>(a); break;
+    case 5: attn_partial_kernel<5><<<grid, block, 0, stream>>>(a); break;
+    case 6: attn_partial_kernel<6><<<grid, block, 0, stream>>>(a); break;
+    case 7: attn_partial_kernel<7><<<grid, block, 0, stream>>>(a); break;
+    default: attn_partial_kernel<8><<<grid, block, 0, stream>>>(a); break;
+    }
     attn_merge_kernel<<<(B * Hq + 3) / 4, 256, 0, stream>>>(a);
     return hipGetLastError();
 }
