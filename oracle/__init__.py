@@ -51,6 +51,7 @@ from .moe import (
 )
 from .block import rms_norm, block_forward, block_forward_per_token
 from .attention import sink_softmax, attn_sink_decode
+from .backward import silu_grad, moe_backward
 
 __all__ = [
     "e2m1_value", "e8m0_value", "mxfp4_dequant", "mxfp4_bits_per_param",
@@ -59,4 +60,5 @@ __all__ = [
     "routing_metadata", "expand_silent", "LayerWeights",
     "rms_norm", "block_forward", "block_forward_per_token",
     "sink_softmax", "attn_sink_decode",
+    "silu_grad", "moe_backward",
 ]
