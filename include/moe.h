@@ -61,7 +61,8 @@ enum {
     MOE_ERR_WORKSPACE = -4, /* workspace smaller than moe_workspace_bytes()      */
     MOE_ERR_ALIGN     = -5, /* a pointer is not 16-byte aligned                  */
     MOE_ERR_HIP       = -6, /* the HIP runtime reported an error at enqueue      */
-    MOE_ERR_STATE     = -7  /* profiling calls out of order                      */
+    MOE_ERR_STATE     = -7, /* profiling calls out of order                      */
+    MOE_ERR_DISABLED  = -8  /* entry point switched off in this build (see it)   */
 };
 
 /* Problem sizes; field names follow the model configs on the pages
@@ -195,6 +196,42 @@ size_t moe_attn_workspace_bytes(const moe_attn_problem *p);
 int moe_attn_sink_decode(const moe_attn_problem *p, const void *q, const void *k_cache, const void *v_cache,
                          const void *sinks, const int32_t *lens, void *out, void *workspace,
                          size_t workspace_bytes, void *stream);
+
+/* Gradients of the layer for fine-tuning ("gpt-oss-40b-64a8-init" page:
+ * section 1, Train Wide, Deploy Narrow; section 5.2, selective gradient
+ * control: original experts frozen while the copies train, the router
+ * trainable throughout).  For an upstream gradient dout [T, H] of out, with
+ * the routing of the moe_forward call that produced out held fixed (the
+ * top-k selection passes no gradient; the selected softmax does):
+ *   d_h [T, H]          input gradient, act dtype, rounded once (NULL: skip)
+ *   grads->d_w_router   [E, H] fp32, grads->d_b_router [E] fp32
+ *   grads->d_w_gate, d_w_up [E, I, H] fp32, grads->d_w_down [E, H, I] fp32
+ * Every gradient pointer may be NULL (not computed).  Outputs are written,
+ * not accumulated.  trainable [E] uint8 device array (NULL: all): experts
+ * with 0 get no expert-matrix gradients (their slices are not written); the
+ * router and d_h are the same either way.  routing must hold the four
+ * arrays moe_forward returned for this h (topk_idx, topk_w, expert_offsets,
+ * perm_src; logits unused).  Supported: act_dtype and expert_dtype MOE_BF16
+ * (else MOE_ERR_DTYPE), the sizes moe_forward takes.  Products in bf16 on
+ * the matrix cores with fp32 accumulation; g, u are recomputed, and
+ * d(gate), d(up), act, p*dout are rounded to bf16 before the products that
+ * take them.  workspace: moe_backward_workspace_bytes(p) bytes, 16-byte
+ * aligned, not to be touched until the stream has passed the call.  T = 0
+ * writes nothing.  Errors: MOE_ERR_NULL (p, w, h, dout, routing or one of its
+ * four arrays, workspace, a weight NULL while T > 0), MOE_ERR_SHAPE,
+ * MOE_ERR_DTYPE, MOE_ERR_WORKSPACE, MOE_ERR_ALIGN (16 bytes for tensors and
+ * workspace, 4 for routing arrays and gradients), MOE_ERR_HIP.
+ * SWITCHED OFF: the first GPU run of these kernels ended in a memory fault
+ * whose cause has not been found (the kernels' index arithmetic checks out
+ * against the buffers on the CPU).  Until it is, every call with T > 0 that
+ * passes the argument checks returns MOE_ERR_DISABLED and enqueues nothing. */
+typedef struct {
+    float *d_w_router, *d_b_router, *d_w_gate, *d_w_up, *d_w_down;
+} moe_grads;
+size_t moe_backward_workspace_bytes(const moe_problem *p);
+int moe_backward(const moe_problem *p, const moe_weights *w, const void *h, const void *d_out,
+                 const moe_routing *routing, const uint8_t *trainable, void *d_h, const moe_grads *grads,
+                 void *workspace, size_t workspace_bytes, void *stream);
 
 /* Silent expansion ("gpt-oss-40b-64a8-init" page, section 2 Principle/Proof,
  * section 5.2): for every per-expert tensor of *src (w_router, b_router,

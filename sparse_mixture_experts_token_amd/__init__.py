@@ -12,6 +12,8 @@ The functions mirror the C entry points of ``include/moe.h``:
 * ``moe_forward(problem, weights, h, out, routing=None, workspace=None)``
 * ``moe_block_workspace_bytes(problem)``
 * ``moe_block_forward(problem, weights, norm_weight, eps, x, out, routing=None, workspace=None)``
+* ``moe_backward_workspace_bytes(problem)``
+* ``moe_backward(problem, weights, h, d_out, routing, d_h=None, grads=None, trainable=None, workspace=None)``
 * ``moe_attn_workspace_bytes(problem)``
 * ``moe_attn_sink_decode(problem, q, k_cache, v_cache, sinks, lens, out, workspace=None)``
 * ``moe_expand_silent(base, src, M, dst)``
@@ -37,9 +39,10 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
 MOE_NUM_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
-          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_HIP", -7: "MOE_ERR_STATE"}
+          -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_HIP", -7: "MOE_ERR_STATE",
+          -8: "MOE_ERR_DISABLED"}
 EXPORTED = ("moe_workspace_bytes", "moe_forward", "moe_block_workspace_bytes", "moe_block_forward",
-            "moe_attn_workspace_bytes", "moe_attn_sink_decode", "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
+            "moe_backward_workspace_bytes", "moe_backward", "moe_attn_workspace_bytes", "moe_attn_sink_decode", "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
             "moe_profile_begin", "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name")
 MOE_PROFILE_ALL = (1 << (MOE_NUM_STAGES + 1)) - 1
 
@@ -57,6 +60,13 @@ class _Problem(ctypes.Structure):
 
 _WEIGHT_FIELDS = ("w_router", "b_router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")
 _ROUTING_FIELDS = ("logits", "topk_idx", "topk_w", "expert_offsets", "perm_src")
+
+
+_GRAD_FIELDS = ("d_w_router", "d_b_router", "d_w_gate", "d_w_up", "d_w_down")
+
+
+class _Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _GRAD_FIELDS]
 
 
 class _AttnProblem(ctypes.Structure):
@@ -125,6 +135,12 @@ def load() -> ctypes.CDLL:
                                       ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.moe_block_forward.restype = ctypes.c_int
+    lib.moe_backward_workspace_bytes.argtypes = [ctypes.POINTER(_Problem)]
+    lib.moe_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_backward.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.POINTER(_Routing), ctypes.c_void_p, ctypes.c_void_p,
+                                 ctypes.POINTER(_Grads), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.moe_backward.restype = ctypes.c_int
     lib.moe_attn_workspace_bytes.argtypes = [ctypes.POINTER(_AttnProblem)]
     lib.moe_attn_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_attn_sink_decode.argtypes = [ctypes.POINTER(_AttnProblem)] + [ctypes.c_void_p] * 7 + [
@@ -246,6 +262,33 @@ def moe_block_forward(problem: Problem, weights: dict, norm_weight, eps: float, 
                                ctypes.byref(r) if r is not None else None, _ptr(workspace), int(workspace_bytes),
                                _stream(stream))
     _check(st)
+
+
+def moe_backward_workspace_bytes(problem: Problem) -> int:
+    p = problem._c()
+    return int(load().moe_backward_workspace_bytes(ctypes.byref(p)))
+
+
+def moe_backward(problem: Problem, weights: dict, h, d_out, routing: dict, d_h=None, grads: dict | None = None,
+                 trainable=None, workspace=None, workspace_bytes: int | None = None, stream=None) -> None:
+    """Enqueue the layer's gradients on ``stream`` (default: torch's current
+    stream).  ``routing`` holds the forward's ``topk_idx``, ``topk_w``,
+    ``expert_offsets`` and ``perm_src``; ``grads`` maps ``d_w_router``,
+    ``d_b_router``, ``d_w_gate``, ``d_w_up``, ``d_w_down`` to fp32 tensors
+    (missing: not computed); ``trainable`` is an [E] uint8 tensor or None."""
+    lib = load()
+    p = problem._c()
+    w = _weights(weights)
+    r = _routing(routing)
+    grads = grads or {}
+    unknown = set(grads) - set(_GRAD_FIELDS)
+    if unknown:
+        raise KeyError(f"unknown gradient fields {sorted(unknown)}")
+    g = _Grads(*[_ptr(grads.get(n)) for n in _GRAD_FIELDS])
+    workspace, workspace_bytes = _workspace(lib.moe_backward_workspace_bytes, p, h, workspace, workspace_bytes)
+    _check(lib.moe_backward(ctypes.byref(p), ctypes.byref(w), _ptr(h), _ptr(d_out),
+                            ctypes.byref(r) if r is not None else None, _ptr(trainable), _ptr(d_h), ctypes.byref(g),
+                            _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def moe_attn_workspace_bytes(problem: AttnProblem) -> int:

@@ -300,6 +300,25 @@ hipError_t launch_down(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H, int k, const void* residual,
                           hipStream_t stream);
 
+// Gradients of the layer (backward.hip).  bf16 activations and expert
+// weights; the routing is the forward's.  Buffers G, U, GY, DA fp32 and Xp,
+// Dp, dY, dG, dU, ACT bf16 are [T k, H or I] workspace regions; dsd [T, Ep]
+// bf16 (Ep = E rounded up to 8), dsf [T, E] fp32; tiles [bwd_max_tiles].
+struct BwdArgs {
+    int T, H, I, E, k;
+    const uint16_t *h, *dout, *w_router, *w_gate, *w_up, *w_down;
+    const int32_t *topk_idx, *offsets, *perm;
+    const float* topk_w;
+    const uint8_t* trainable;
+    uint16_t* dh;
+    float *dw_router, *db_router, *dw_gate, *dw_up, *dw_down;
+    int32_t *inv, *tiles, *ntiles;
+    uint16_t *Xp, *Dp, *dY, *dG, *dU, *ACT, *dsd;
+    float *G, *U, *GY, *DA, *dp, *dsf;
+};
+int bwd_max_tiles(int T, int k, int E);
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);
+
 // Decode attention with learned sinks (attn_sink.hip).  Shapes: Hq a multiple
 // of Hkv with at most 8 query heads per key/value head, D a multiple of 8 up
 // to 64, Tk >= 1, window >= 0 (0: all keys).

@@ -36,7 +36,7 @@ import numpy as np
 ROOT_SEED = 20261203
 
 # tensor ids of the per-tensor streams
-TID_H, TID_WR, TID_BR, TID_GATE, TID_UP, TID_DOWN, TID_HOT, TID_ROWSCALE, TID_NORM, TID_ATTN = range(10)
+TID_H, TID_WR, TID_BR, TID_GATE, TID_UP, TID_DOWN, TID_HOT, TID_ROWSCALE, TID_NORM, TID_ATTN, TID_DOUT = range(11)
 
 
 @dataclass(frozen=True)
@@ -260,6 +260,11 @@ def attn_inputs(seed: int, B: int, Hq: int, Hkv: int, Tk: int, D: int) -> dict:
         lens[1] = 1
     out["lens"] = lens
     return out
+
+
+def grad_output(seed: int, T: int, H: int) -> np.ndarray:
+    """Seeded upstream gradient of the layer output: [T, H] N(0, 1) in bf16 bits."""
+    return f32_to_bf16_bits(rng_for(seed, TID_DOUT).standard_normal((T, H), dtype=np.float32))
 
 
 def decode_T(key: int) -> int:

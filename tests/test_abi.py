@@ -20,7 +20,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = smoe.load()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(smoe.EXPORTED) == names
@@ -101,6 +101,34 @@ def test_block_argument_errors_return_before_any_launch():
     # T = 0 is a no-op even with no buffers at all
     assert _block(smoe.Problem(0, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_BF16), g=0, x=0, out=0, ws=0,
                   ws_bytes=0) == 0
+
+
+def test_backward_argument_errors_return_before_any_launch():
+    lib = smoe.load()
+    P = smoe.Problem(8, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_BF16)
+    w = smoe._Weights(0x1000, 0x1100, 0x2000, 0x3000, 0x4000, None, None, None)
+    r = smoe._Routing(None, 0x5000, 0x5100, 0x5200, 0x5300)
+    g = smoe._Grads(0x6000, 0x6100, 0x6200, 0x6300, 0x6400)
+    need = lib.moe_backward_workspace_bytes(ctypes.byref(P._c()))
+    assert need > 0
+
+    def call(p=P, w=w, h=0x7000, d=0x7100, r=r, tr=None, dh=0x7200, g=g, ws=0x8000, nb=need):
+        return lib.moe_backward(ctypes.byref(p._c()), ctypes.byref(w) if w is not None else None, h, d,
+                                ctypes.byref(r) if r is not None else None, tr, dh, ctypes.byref(g), ws, nb, None)
+
+    assert call(p=smoe.Problem(8, 64, 128, 4, 2, smoe.MOE_F32, smoe.MOE_F32)) == -3
+    assert call(p=smoe.Problem(8, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_MXFP4)) == -3
+    assert call(p=smoe.Problem(8, 60, 128, 4, 2)) == -2
+    assert call(h=0) == -1 and call(d=0) == -1 and call(r=None) == -1 and call(ws=0) == -1
+    assert call(r=smoe._Routing(None, 0x5000, None, 0x5200, 0x5300)) == -1
+    assert call(nb=need - 1) == -4
+    assert call(h=0x7008) == -5 and call(dh=0x7208) == -5
+    assert call(g=smoe._Grads(0x6002, None, None, None, None)) == -5
+    # T = 0 writes nothing and needs no buffers
+    assert call(p=smoe.Problem(0, 64, 128, 4, 2), h=0, d=0, r=None, dh=0, ws=0, nb=0) == 0
+    # switched off: a call that passes every check enqueues nothing
+    assert call() == -8
+    assert "switched off" in smoe.moe_status_string(-8)
 
 
 def test_attention_argument_errors_return_before_any_launch():
