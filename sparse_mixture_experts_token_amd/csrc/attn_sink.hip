@@ -11,20 +11,20 @@
 // Two kernels.  attn_partial_kernel: one workgroup per (sequence, key/value
 // head, chunk of the visible keys), so that short batches still fill the
 // chip; the group's G query heads share every key and value load.  The chunk
-// is cut into 64-key tiles dealt round-robin to four waves.  Per tile, all 16
+// is cut into 64-key tiles dealt round-robin to four waves.  Per tile, all 24
 // loads of a lane are issued first, then:
-//   scores - a 16x16x32 bf16 MFMA per 16 keys and 32 features: the G query
-//            heads are the A rows (padded to 16 with zeros), the key rows
-//            the B columns, read from HBM straight into operand layout;
-//   softmax - running max m and sum l per head (streaming softmax), reduced
-//            over the 16 lanes that hold a head's keys; the weights go to
-//            LDS as [key][head], with the factor that rescales the sums;
-//   values  - lane (kq, dc) = (l / 8, l % 8) holds 16 bytes (features
-//            8dc..8dc+7) of value row 8r + kq, so one load covers 8 whole
-//            128-byte rows; p * v is added into per-lane fp32 sums, reduced
-//            over kq at the end.  (The MFMA would need the value tile
-//            transposed, key-major per feature; on the vector unit it is
-//            about 600 instructions per tile, under the time of its loads.)
+//   scores - S^T = K Q^T on 16x16x32 bf16 MFMAs, 16 keys per product: the
+//            key rows are the A rows, read from HBM straight into operand
+//            layout; the G query heads are the B columns (zero-padded to 16).
+//            Lane (col, grp) = (l % 16, l / 16) ends up holding the scores of
+//            head col for the 16 keys 16blk + 4grp + j;
+//   softmax - running max m and sum l of head col (streaming softmax),
+//            reduced over the 4 lanes that share the head;
+//   values  - O^T += V^T P^T on 16x16x4 fp32 MFMAs, one 4-key step per
+//            (blk, j): a lane's own fp32 weight is its B element, and its A
+//            element is feature 4col + mb of the step's key row, so one
+//            8-byte load per step feeds the four 16-feature blocks mb.
+//            Nothing is transposed and the weights stay in fp32.
 // The four waves are merged and the chunk's (m, l, sum p v) written to the
 // workspace.  attn_merge_kernel: per (sequence, query head), the chunks are
 // combined with the sink as the starting state (m = sink, l = 1, nothing in
@@ -76,56 +76,49 @@ __device__ __forceinline__ void visible(const AttnArgs& a, int b, int& lo, int& 
 // G query heads share each key/value head (G <= 8); one instantiation per G.
 template <int G>
 __global__ __launch_bounds__(kAWaves * 64) void attn_partial_kernel(AttnArgs a) {
-    __shared__ __align__(16) float s_p[kAWaves][kATile][8];  // this tile's weights, [key][head]
-    __shared__ __align__(16) float s_corr[kAWaves][8];       // this tile's rescale factor per head
-    __shared__ float s_m[kAWaves][G], s_l[kAWaves][G];
-    __shared__ float s_acc[kAWaves][G][kAMaxD];
+    __shared__ float s_m[kAWaves][16], s_l[kAWaves][16];
+    __shared__ float s_acc[kAWaves][16][kAMaxD];  // [wave][head][feature]
     const int c = blockIdx.x % a.nchunk;
     const int bg = blockIdx.x / a.nchunk;
     const int b = bg / a.Hkv, g = bg - (bg / a.Hkv) * a.Hkv;
     const int D = a.D;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int col = lane & 15, grp = lane >> 4;  // MFMA column (key) and row group (heads 4grp..4grp+3)
-    const int kq = lane >> 3, dc = lane & 7;     // value layout: key 8r+kq, features 8dc..8dc+7
-    const bool dlive = 8 * dc < D;
+    const int col = lane & 15, grp = lane >> 4;  // head column; key / feature row group
     int lo, n;
     visible(a, b, lo, n);
     const int kb = lo + c * a.chunk;
     const int ke = min(n, kb + a.chunk);
     const size_t kv0 = ((size_t)b * a.Hkv + g) * a.Tk;
 
-    // Q as the MFMA A operand: row = head (rows G..15 zero), K = features;
-    // K step ks covers features 32ks..32ks+31, lane's 8 at 32ks + 8grp.
-    bf16x8 qa[2];
+    // Scores are S^T = K Q^T (16x16x32 bf16): A = key rows (row = key, K =
+    // features 8grp + 32ks ..+7), B = Q^T (column = head col, zero for col >= G).
+    bf16x8 qb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int f = 32 * ks + 8 * grp;
-        qa[ks] = bf16x8{};
+        qb[ks] = bf16x8{};
         if (col < G && f < D)
-            qa[ks] = *reinterpret_cast<const bf16x8*>(a.q + ((size_t)b * a.Hq + g * G + col) * D + f);
+            qb[ks] = *reinterpret_cast<const bf16x8*>(a.q + ((size_t)b * a.Hq + g * G + col) * D + f);
     }
     const bool ks1 = D > 32;  // uniform
     const int fk0 = 8 * grp < D ? 8 * grp : 0, fk1 = 32 + 8 * grp < D ? 32 + 8 * grp : 0;
     const bool klive0 = 8 * grp < D, klive1 = 32 + 8 * grp < D;
-    const int fv = 8 * (dlive ? dc : 0);
+    // Values: lane reads features 4col..4col+3 of a row (one per 16-feature block mb).
+    const bool vlive = 4 * col < D;
+    const int fv = vlive ? 4 * col : 0;
 
-    float m[4], l[4], acc[G][8];
+    // Running max and sum of head col (equal in the 4 lanes col + 16 grp);
+    // acc[mb][j] = O^T[feature 4(4grp + j) + mb][head col].
+    float m = kNegInf, l = 0.0f;
+    f32x4 acc[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        m[j] = kNegInf;
-        l[j] = 0.0f;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] = 0.0f;
+    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     for (int t0 = kb + wave * kATile; t0 < ke; t0 += kAWaves * kATile) {  // wave-uniform
-        // key rows as the B operand (column = key t0 + 16blk + col) and value
-        // rows in the value layout, all issued before any is used.  Rows past
-        // the chunk read key t0 (visible) and are masked below.
+        // Key t0 + 16blk + col as an A row; value row t0 + 16blk + 4grp + j.
+        // Rows past the chunk read key t0 (visible) and get weight 0.
         bf16x8 kr[4][2];
-        uint4 vr[8];
+        uint2 vr[4][4];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             const int j = t0 + 16 * blk + col;
@@ -134,99 +127,72 @@ __global__ __launch_bounds__(kAWaves * 64) void attn_partial_kernel(AttnArgs a) 
             kr[blk][1] = ks1 ? *reinterpret_cast<const bf16x8*>(row + fk1) : bf16x8{};
         }
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int j = t0 + 8 * r + kq;
-            vr[r] = *reinterpret_cast<const uint4*>(a.v + (kv0 + (j < ke ? j : t0)) * D + fv);
-        }
-        // scores: D[j] of block blk = q[head 4grp+j] . k[key t0+16blk+col]
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j = t0 + 16 * blk + 4 * grp + jj;
+                vr[blk][jj] = *reinterpret_cast<const uint2*>(a.v + (kv0 + (j < ke ? j : t0)) * D + fv);
+            }
+        // s[blk][jj]: score of head col and key t0 + 16blk + 4grp + jj
         float s[4][4];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
             f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
-            d = mfma16(qa[0], klive0 ? kr[blk][0] : bf16x8{}, d);
-            if (ks1) d = mfma16(qa[1], klive1 ? kr[blk][1] : bf16x8{}, d);
-            const bool valid = t0 + 16 * blk + col < ke;
+            d = mfma16(klive0 ? kr[blk][0] : bf16x8{}, qb[0], d);
+            if (ks1) d = mfma16(klive1 ? kr[blk][1] : bf16x8{}, qb[1], d);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s[blk][j] = valid ? d[j] * a.scale : kNegInf;
+            for (int jj = 0; jj < 4; ++jj)
+                s[blk][jj] = t0 + 16 * blk + 4 * grp + jj < ke ? d[jj] * a.scale : kNegInf;
         }
-        // streaming softmax per head over the tile's 64 keys (16 lanes x 4 blocks)
-        float corr[4];
+        // streaming softmax of head col over the tile's 64 keys (16 here x 4 lanes)
+        float mx = s[0][0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float mx = fmaxf(fmaxf(s[0][j], s[1][j]), fmaxf(s[2][j], s[3][j]));
+        for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-            for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-            const float mn = fmaxf(m[j], mx);  // finite: key t0 is in every 16-lane group
-            corr[j] = __expf(m[j] - mn);
-            float sum = 0.0f;
+            for (int jj = 0; jj < 4; ++jj) mx = fmaxf(mx, s[blk][jj]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m, mx);  // finite: key t0 is in lane col's registers
+        const float corr = __expf(m - mn);
+        float sum = 0.0f;
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-                const float p = s[blk][j] == kNegInf ? 0.0f : __expf(s[blk][j] - mn);
-                s[blk][j] = p;
+        for (int blk = 0; blk < 4; ++blk)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float p = s[blk][jj] == kNegInf ? 0.0f : __expf(s[blk][jj] - mn);
+                s[blk][jj] = p;
                 sum += p;
             }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        l = l * corr + sum;
+        m = mn;
 #pragma unroll
-            for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
-            l[j] = l[j] * corr[j] + sum;
-            m[j] = mn;
-        }
-        if (lane < 32) {  // heads 0..7; rows 8..15 are padding
+        for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk)
-                *reinterpret_cast<float4*>(&s_p[wave][16 * blk + col][4 * grp]) =
-                    float4{s[blk][0], s[blk][1], s[blk][2], s[blk][3]};
-            if (col == 0) *reinterpret_cast<float4*>(&s_corr[wave][4 * grp]) = float4{corr[0], corr[1], corr[2], corr[3]};
-        }
-        __builtin_amdgcn_wave_barrier();
-        // weighted values: acc[h][e] (features 8dc+e, keys kq mod 8) on VALU
-        {
-            const float4 c0 = *reinterpret_cast<const float4*>(&s_corr[wave][0]);
-            const float4 c1 = *reinterpret_cast<const float4*>(&s_corr[wave][4]);
-            const float cr[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            for (int e = 0; e < 4; ++e) acc[mb][e] *= corr;
+        // O^T += V^T P^T, 16x16x4 fp32, one K step per (blk, jj): lane (col, grp)
+        // gives V[key 16blk + 4grp + jj][feature 4col + mb] (A) and its own
+        // weight P[head col][that key] (B).
 #pragma unroll
-            for (int h = 0; h < G; ++h)
+        for (int blk = 0; blk < 4; ++blk)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] *= cr[h];
-        }
+            for (int jj = 0; jj < 4; ++jj) {
+                const uint2 w = vlive ? vr[blk][jj] : uint2{0u, 0u};
+                const float vf[4] = {bf16_bits_to_f32(w.x & 0xffffu), bf16_bits_to_f32(w.x >> 16),
+                                     bf16_bits_to_f32(w.y & 0xffffu), bf16_bits_to_f32(w.y >> 16)};
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            float vf[8];
-            unpack8(dlive ? vr[r] : uint4{0u, 0u, 0u, 0u}, vf);  // invalid keys have p = 0
-            const float4 p0 = *reinterpret_cast<const float4*>(&s_p[wave][8 * r + kq][0]);
-            const float4 p1 = *reinterpret_cast<const float4*>(&s_p[wave][8 * r + kq][4]);
-            const float pr[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
-        }
-        __builtin_amdgcn_wave_barrier();  // weights read before the next tile writes them
-    }
-    // sum the per-lane values over the 8 key lanes kq (lanes dc, dc+8, ..., dc+56)
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float x = acc[h][e];
-            x += __shfl_xor(x, 8, 64);
-            x += __shfl_xor(x, 16, 64);
-            x += __shfl_xor(x, 32, 64);
-            acc[h][e] = x;
-        }
-        if (kq == 0 && dlive) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) s_acc[wave][h][8 * dc + e] = acc[h][e];
-        }
-    }
-    if (lane < 32 && col == 0) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (4 * grp + j < G) {
-                s_m[wave][4 * grp + j] = m[j];
-                s_l[wave][4 * grp + j] = l[j];
+                for (int mb = 0; mb < 4; ++mb) acc[mb] = mfma16(vf[mb], s[blk][jj], acc[mb]);
             }
-        }
     }
+    if (grp == 0) {
+        s_m[wave][col] = m;
+        s_l[wave][col] = l;
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_acc[wave][col][4 * (4 * grp + e) + mb] = acc[mb][e];
     __syncthreads();
     if (wave != 0) return;
     for (int h = 0; h < G; ++h) {
