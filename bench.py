@@ -14,8 +14,10 @@ TFLOP/s and fraction of the bf16 MFMA peak, the roofline of the dominant
 kernel (the gate/up grouped GEMM, its launch duration from HIP events recorded
 around it on the launch stream during the timed steps), per-stage times from a
 second pass that records every stage boundary, a decode measurement (T = 64,
-the first 64 rows) against the HBM roofline, and the fp64 CPU reference timed
-on a bounded sample of the same workload.
+the first 64 rows) against the HBM roofline, the fp64 CPU reference timed
+on a bounded sample of the same workload, and decode attention with sinks at
+the gpt-oss-20b head shape against the HBM roofline (with its fp64 reference
+timed on the same workload).
 """
 from __future__ import annotations
 
@@ -100,7 +102,7 @@ def cpu_baseline(key, T_sample):
                       f"expert weights generated and widened on the fly; {dt:.1f} s"}
 
 
-def attention_leg(smoe, torch, dev, steps):
+def attention_leg(smoe, torch, dev, steps, cpu=True):
     """Decode attention with sinks at the gpt-oss-20b head shape (64 query
     heads, 8 key/value heads, head dim 64): 64 sequences of 4096 cached keys,
     full attention, seeded N(0, 1) bf16 inputs.  HBM roofline on the bytes the
@@ -130,10 +132,34 @@ def attention_leg(smoe, torch, dev, steps):
     ms = e0.elapsed_time(e1) / steps
     byts = 2 * B * Hkv * Tk * D * 2 + 2 * B * Hq * D * 2 + Hq * 2
     gbps = byts / (ms * 1e-3) / 1e9
-    return {"workload": f"decode attention with sinks, {B} sequences x {Tk} keys, {Hq} query / {Hkv} kv heads, "
-                        f"head dim {D}, full, bf16", "ms_per_step": round(ms, 4), "alg_bytes": byts,
-            "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
-            "kernels": "attn_partial_kernel + attn_merge_kernel"}
+    res = {"workload": f"decode attention with sinks, {B} sequences x {Tk} keys, {Hq} query / {Hkv} kv heads, "
+                       f"head dim {D}, full, bf16", "ms_per_step": round(ms, 4), "alg_bytes": byts,
+           "hbm_GBps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+           "sequences_per_s": round(B / (ms * 1e-3), 1), "kernels": "attn_partial_kernel + attn_merge_kernel"}
+    if cpu:
+        res["cpu_baseline"] = attention_cpu_baseline(Hq, Hkv, Tk, D, n_seq=B)
+    return res
+
+
+def attention_cpu_baseline(Hq, Hkv, Tk, D, n_seq):
+    """The fp64 attention reference as it stands on n_seq sequences of the
+    same shape (seeded N(0, 1) bf16 inputs, every key visible)."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    inp = synth.attn_inputs(20261203, n_seq, Hq, Hkv, Tk, D)
+    w = lambda a: oracle.widen(a, "bf16")
+    q, k, v, sinks = w(inp["q"]), w(inp["k"]), w(inp["v"]), w(inp["sinks"])
+    t0 = time.perf_counter()
+    oracle.attn_sink_decode(q, k, v, sinks, np.full(n_seq, Tk), 0, 1.0 / np.sqrt(D))
+    dt = time.perf_counter() - t0
+    return {"value": round(n_seq / dt, 2), "unit": "sequences/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_seq} sequences of {Tk} keys (the whole workload), fp64 NumPy, one (sequence, head) "
+                      f"at a time; {dt:.2f} s"}
 
 
 def main():
@@ -246,7 +272,7 @@ def main():
               "stage_ms_profiled_pass": [round(x / dcalls, 5) for x in dstage]}
 
     del wsd, outd, hd
-    attention = attention_leg(smoe, torch, dev, args.attn_steps)
+    attention = attention_leg(smoe, torch, dev, args.attn_steps, cpu=not args.no_cpu_baseline)
 
     cpu = None
     if not args.no_cpu_baseline:
