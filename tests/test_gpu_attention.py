@@ -2,7 +2,9 @@
 with the fp64 reference ``oracle.attn_sink_decode``: outputs within relative
 L2 5e-3 and max abs 1e-2*max|ref| (bf16 output), on seeded N(0, 1) inputs with
 ragged sequence lengths, full and local (128-key) attention, scale 1/sqrt(D);
-the explainer's worked example bit for bit."""
+edge shapes (one key, D = 8 and 24 and 40, one to eight query heads per
+key/value head, a window longer than the cache, more than 1024 groups); the
+explainer's worked example bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -36,12 +38,16 @@ def reference(P, inp, lens=True):
 
 
 CASES = [(1, 4, 64, 8, 300, 64, 0), (2, 4, 64, 8, 300, 64, 128), (3, 8, 64, 8, 4096, 64, 0),
-         (4, 8, 64, 8, 4096, 64, 128), (5, 3, 4, 2, 37, 16, 0), (6, 5, 8, 8, 70, 32, 16)]
+         (4, 8, 64, 8, 4096, 64, 128), (5, 3, 4, 2, 37, 16, 0), (6, 5, 8, 8, 70, 32, 16),
+         (9, 1, 8, 8, 1, 8, 0), (10, 2, 16, 2, 100, 64, 200), (11, 3, 6, 3, 513, 24, 0),
+         (12, 130, 64, 8, 33, 64, 0), (13, 2, 7, 1, 1000, 40, 300)]
 
 
 @pytest.mark.parametrize("seed,B,Hq,Hkv,Tk,D,window", CASES,
                          ids=["20b-300-full", "20b-300-local128", "20b-4096-full", "20b-4096-local128",
-                              "fixture-heads-16d", "no-sharing-32d-local16"])
+                              "fixture-heads-16d", "no-sharing-32d-local16", "one-key-8d",
+                              "window-longer-than-cache", "two-heads-per-group-24d-ragged",
+                              "1040-groups-one-chunk", "seven-heads-one-kv-40d-local300"])
 def test_attention_parity(seed, B, Hq, Hkv, Tk, D, window):
     P = smoe.AttnProblem(B, Hq, Hkv, Tk, D, window)
     inp = synth.attn_inputs(seed, B, Hq, Hkv, Tk, D)
