@@ -39,6 +39,17 @@ METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (prefill), % HBM GB/s (decode)"
 DOMINANT_STAGE = 2          # gate/up grouped GEMM
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_c2_prefill_traffic.json")
 
+# The other layers the method is quoted on: (synth config key, tokens, silent
+# expansion factor of the gpt-oss-20b layer or 0, description).
+OTHER_WORKLOADS = {
+    "c3-64a8": (3, 4096, 0, "random 64-expert top-8 layer (64a8 shape), prefill T=4096, bf16"),
+    "c3-96a12": (2, 4096, 3, "gpt-oss-20b layer silently expanded x3 (96a12), top-12, prefill T=4096, bf16"),
+    "c4": (4, 8192, 0, "gpt-oss-120b-shaped layer (128 experts, top-4), MXFP4 experts, 8 hot experts ~50% of "
+                       "assignments, prefill T=8192"),
+    "c5": (5, 2048, 0, "220a20b-shaped layer (248 experts, top-20), MXFP4 experts, prefill T=2048"),
+    "c5-decode": (5, 32, 0, "220a20b-shaped layer (248 experts, top-20), MXFP4 experts, decode T=32"),
+}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -49,6 +60,9 @@ def parse():
     ap.add_argument("--attn-steps", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--workload", default="c2",
+                    help="c2 (default: the contract line) or a comma-separated list of "
+                         + ", ".join(OTHER_WORKLOADS) + " (one JSON line each)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (reference for HBM byte counters)")
     return ap.parse_args()
@@ -162,12 +176,106 @@ def attention_cpu_baseline(Hq, Hkv, Tk, D, n_seq):
                       f"at a time; {dt:.2f} s"}
 
 
+def other_workloads(names, args):
+    """One JSON line per named workload: warmup, then args.steps timed steps
+    with no events (wall clock around the whole loop), then a second pass with
+    an event at every stage boundary for the split.  Prefill lines report
+    layer TFLOP/s against the bf16 MFMA peak; decode lines report the touched
+    experts' weight bytes (MXFP4: 4.25 bits per parameter) against 8 TB/s."""
+    import torch
+    import sparse_mixture_experts_token_amd as smoe
+    import synth
+
+    dev = torch.device("cuda:0")
+    DT = {"f32": smoe.MOE_F32, "bf16": smoe.MOE_BF16, "mxfp4": smoe.MOE_MXFP4}
+    layers = {}
+
+    def tod(a, fmt):
+        if fmt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    for name in names:
+        key, T, M, desc = OTHER_WORKLOADS[name]
+        print(f"[bench] {name}", file=sys.stderr, flush=True)
+        if key not in layers:
+            layers.clear()
+            torch.cuda.empty_cache()
+            L = synth.make_layer(key)
+            st = L.stacked()
+            c = L.cfg
+            w = {"w_router": tod(L.w_router, c.act), "b_router": tod(L.b_router, c.act)}
+            for n in ("gate", "up", "down"):
+                w["w_" + n] = tod(st[n], c.expert)
+                if c.expert == "mxfp4":
+                    w["s_" + n] = tod(st["s_" + n], "u8")
+            del st
+            layers[key] = (L, w)
+        L, w = layers[key]
+        c = L.cfg
+        E, k = c.E, c.k
+        if M > 1:  # silent expansion on the device: every expert tensor repeated M times
+            base = smoe.Problem(0, c.H, c.I, E, k, DT[c.act], DT[c.expert])
+            w = {n: torch.empty((M * t.shape[0],) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+                 for n, t in layers[key][1].items()}
+            smoe.moe_expand_silent(base, layers[key][1], M, w)
+            E, k = M * E, M * k
+        prob = smoe.Problem(T, c.H, c.I, E, k, DT[c.act], DT[c.expert])
+        h = tod(L.h[:T], c.act)
+        out = torch.empty((T, c.H), dtype=h.dtype, device=dev)
+        nb = smoe.moe_workspace_bytes(prob)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+
+        def step():
+            smoe.moe_forward(prob, w, h, out, routing={"expert_offsets": offs}, workspace=ws, workspace_bytes=nb)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        smoe.moe_profile_begin(args.steps)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        stage_ms, calls = smoe.moe_profile_end()
+        F = layer_flops(T, c.H, c.I, E, k)
+        res = {"metric": METRIC, "value": round(T / dt, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 4), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+               "config": {"workload": desc, "T": T, "hidden": c.H, "intermediate": c.I, "experts": E, "top_k": k,
+                          "experts_format": c.expert},
+               "layer_tflops": round(F / dt / 1e12, 2), "layer_mfma_frac": round(F / dt / 1e12 / PEAK_BF16_TFLOPS, 4),
+               "stage_ms_profiled_pass": {smoe.moe_stage_name(i): round(x / calls, 5)
+                                          for i, x in enumerate(stage_ms)}}
+        if T <= 64:
+            counts = np.diff(offs.cpu().numpy())
+            per_expert = 3 * c.H * c.I * (17 / 32 if c.expert == "mxfp4" else 2)
+            Bd = int((counts > 0).sum() * per_expert) + E * c.H * 2 + E * 2 + 2 * T * c.H * 2
+            res["decode"] = {"experts_touched": int((counts > 0).sum()), "alg_bytes": Bd,
+                             "hbm_GBps": round(Bd / dt / 1e9, 1), "hbm_frac": round(Bd / dt / 1e9 / PEAK_HBM_GBPS, 4)}
+        print(json.dumps(res), flush=True)
+        del w, h, out, ws
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.workload != "c2":
+        names = args.workload.split(",")
+        unknown = [n for n in names if n not in OTHER_WORKLOADS]
+        if unknown:
+            print(json.dumps({"error": f"unknown workload(s) {unknown}", "known": ["c2"] + list(OTHER_WORKLOADS)}))
+            sys.exit(2)
+        other_workloads(names, args)
+        return
 
     import torch
     import sparse_mixture_experts_token_amd as smoe
