@@ -374,9 +374,32 @@ def main():
     dstage, dcalls = smoe.moe_profile_end()
     counts_d = np.diff(offd.cpu().numpy())
     Bd = weight_bytes_touched(counts_d, H, I, 2) + E * H * 2 + E * 2 + 2 * Td * H * 2
+    # ... and cold: a 1 GiB read before every step evicts the weights from
+    # the 256 MB Infinity Cache (a read, so the evicted lines are clean and
+    # cost no write-back inside the step); the reads are timed alone and
+    # subtracted
+    flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    n_cold = max(1, args.decode_steps // 4)
+    for _ in range(3):
+        torch.sum(flush, dim=0, out=sink)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(n_cold):
+        torch.sum(flush, dim=0, out=sink)
+        dstep()
+    torch.cuda.synchronize()
+    t_both = time.perf_counter() - t2
+    t3 = time.perf_counter()
+    for _ in range(n_cold):
+        torch.sum(flush, dim=0, out=sink)
+    torch.cuda.synchronize()
+    cold = (t_both - (time.perf_counter() - t3)) / n_cold
+    del flush, sink
     decode = {"workload": f"first {Td} tokens, same layer", "tokens_per_s": round(Td / ddt, 1),
               "ms_per_step": round(ddt * 1e3, 4), "alg_bytes": Bd, "hbm_GBps": round(Bd / ddt / 1e9, 1),
               "hbm_frac": round(Bd / ddt / 1e9 / PEAK_HBM_GBPS, 4),
+              "cold_ms_per_step": round(cold * 1e3, 4), "cold_hbm_frac": round(Bd / cold / 1e9 / PEAK_HBM_GBPS, 4),
               "stage_ms_profiled_pass": [round(x / dcalls, 5) for x in dstage]}
 
     del wsd, outd, hd
