@@ -40,7 +40,8 @@ DOMINANT_STAGE = 2          # gate/up grouped GEMM
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_c2_prefill_traffic.json")
 
 # The other layers the method is quoted on: (synth config key, tokens, silent
-# expansion factor of the gpt-oss-20b layer or 0, description).
+# expansion factor of the gpt-oss-20b layer, 0 for none or -1 for the
+# pre-normalised block around the layer, description).
 OTHER_WORKLOADS = {
     "c3-64a8": (3, 4096, 0, "random 64-expert top-8 layer (64a8 shape), prefill T=4096, bf16"),
     "c3-96a12": (2, 4096, 3, "gpt-oss-20b layer silently expanded x3 (96a12), top-12, prefill T=4096, bf16"),
@@ -48,7 +49,12 @@ OTHER_WORKLOADS = {
                        "assignments, prefill T=8192"),
     "c5": (5, 2048, 0, "220a20b-shaped layer (248 experts, top-20), MXFP4 experts, prefill T=2048"),
     "c5-decode": (5, 32, 0, "220a20b-shaped layer (248 experts, top-20), MXFP4 experts, decode T=32"),
+    "block-c2": (2, 4096, -1, "pre-normalised block x + MoE(RMSNorm(x)) on the gpt-oss-20b layer, prefill T=4096, "
+                              "bf16, eps 1e-5"),
+    "block-c2-decode": (2, 64, -1, "pre-normalised block x + MoE(RMSNorm(x)) on the gpt-oss-20b layer, decode T=64, "
+                                   "bf16, eps 1e-5"),
 }
+BLOCK_EPS = 1e-5
 
 
 def parse():
@@ -221,14 +227,24 @@ def other_workloads(names, args):
             smoe.moe_expand_silent(base, layers[key][1], M, w)
             E, k = M * E, M * k
         prob = smoe.Problem(T, c.H, c.I, E, k, DT[c.act], DT[c.expert])
-        h = tod(L.h[:T], c.act)
-        out = torch.empty((T, c.H), dtype=h.dtype, device=dev)
-        nb = smoe.moe_workspace_bytes(prob)
-        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
         offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        if M < 0:  # the pre-normalised block: x = h with rows rescaled, gain g
+            x_np, g_np = synth.block_inputs(L)
+            h, gain = tod(x_np[:T], c.act), tod(g_np, c.act)
+            nb = smoe.moe_block_workspace_bytes(prob)
+        else:
+            h = tod(L.h[:T], c.act)
+            nb = smoe.moe_workspace_bytes(prob)
+        out = torch.empty((T, c.H), dtype=h.dtype, device=dev)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev)
 
         def step():
-            smoe.moe_forward(prob, w, h, out, routing={"expert_offsets": offs}, workspace=ws, workspace_bytes=nb)
+            if M < 0:
+                smoe.moe_block_forward(prob, w, gain, BLOCK_EPS, h, out, routing={"expert_offsets": offs},
+                                       workspace=ws, workspace_bytes=nb)
+            else:
+                smoe.moe_forward(prob, w, h, out, routing={"expert_offsets": offs}, workspace=ws,
+                                 workspace_bytes=nb)
 
         for _ in range(args.warmup):
             step()
