@@ -60,6 +60,7 @@ constexpr int kWM = kWaves / 2;   // waves along the rows (2 along the weight ro
 constexpr int kBM = 256;          // rows per tile: 8 groups of 32, 2 per wave
 constexpr int kBK = 64;      // K per LDS stage: 128 bytes of each row
 constexpr int kXcds = 8;
+static_assert(kXcds == kXcdRanges, "the route scan cuts one work range per XCD");
 constexpr int kBNGateUp = 128;
 constexpr int kBNDown = 256;
 constexpr int kStagesGateUp = 2;  // 64 KB stages
@@ -76,6 +77,7 @@ struct BArgs {
     const Tile* tiles;
     const int32_t* work;    // row tile * n_ntiles + column tile, expert-grouped order
     const int32_t* n_work;
+    const int32_t* bounds;  // [kXcdRanges + 1]
     int32_t* queue;         // [8] per-XCD work counters, zero at launch
     void* out;
     uint32_t a_bytes;
@@ -494,8 +496,9 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
 }
 
 // Persistent workgroups, one per CU.  Blocks are dealt round-robin to the 8
-// XCDs; XCD x owns the x-th of 8 equal contiguous ranges of the work list
-// (sized by the actual item count) and its workgroups take the range's items
+// XCDs; XCD x owns the x-th of 8 contiguous ranges of the work list, cut by
+// the route scan so that their estimated costs are equal (a short row tile
+// costs less than a full one), and its workgroups take the range's items
 // in order from the XCD's counter, so a workgroup that drew cheap items (the
 // short last row tile of an expert) takes more of them, and the row tiles
 // sharing a weight tile still run together on one XCD.
@@ -503,10 +506,9 @@ template <int MODE, int BN, int S, bool MXW>
 __device__ __forceinline__ void gemm_body(const BArgs& args) {
     __shared__ int s_q;
     const int n_work = args.n_work[0];
-    const int per_xcd = (n_work + kXcds - 1) / kXcds;
     const int xcd = blockIdx.x % kXcds;
-    const int base = xcd * per_xcd;
-    const int end = min(base + per_xcd, n_work);
+    const int base = min(max(args.bounds[xcd], 0), n_work);
+    const int end = min(max(args.bounds[xcd + 1], base), n_work);
     for (;;) {
         if (threadIdx.x == 0) s_q = base + atomicAdd(args.queue + xcd, 1);
         // s_q visible to every wave, and every wave done with the previous item's LDS
@@ -552,6 +554,7 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.N = p.I;
         a.work = p.work_gateup;
         a.n_work = p.n_work_gateup;
+        a.bounds = p.bounds_gateup;
         a.queue = p.queues;
         a.n_ntiles = (p.I + kBNGateUp - 1) / kBNGateUp;
     } else {
@@ -566,6 +569,7 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.N = p.H;
         a.work = p.work_down;
         a.n_work = p.n_work_down;
+        a.bounds = p.bounds_down;
         a.queue = p.queues + kXcds;
         a.n_ntiles = (p.H + kBNDown - 1) / kBNDown;
     }

@@ -69,7 +69,8 @@ Layout layout(const moe_problem* p, int router_dt = -1, bool all_plogits = false
     L.perm = o;     o = align_up(o + tk * 4);
     L.inv = o;      o = align_up(o + tk * 4);
     L.tiles = o;    o = align_up(o + (size_t)L.max_tiles * sizeof(Tile));
-    L.ntiles = o;   o = align_up(o + 16);  // tile count, then the two work-list counts
+    L.ntiles = o;   o = align_up(o + 256);  // tile count, the two work-list counts, then at ints 16 and 32
+                                            // the two lists' XCD range bounds
     L.queues = o;   o = align_up(o + moe::kNumQueues * 4);
     // column tiles of the prefill work lists (the decode kernels need none)
     // (only the bf16-activation prefill kernels walk work lists)
@@ -233,8 +234,8 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     };
 
     hipError_t e = hipSuccess;
-    moe::WorkList wl0{L.lists ? (int32_t*)(ws + L.work0) : nullptr, ntiles + 1, L.nc0};
-    moe::WorkList wl1{L.lists ? (int32_t*)(ws + L.work1) : nullptr, ntiles + 2, L.nc1};
+    moe::WorkList wl0{L.lists ? (int32_t*)(ws + L.work0) : nullptr, ntiles + 1, L.nc0, ntiles + 16};
+    moe::WorkList wl1{L.lists ? (int32_t*)(ws + L.work1) : nullptr, ntiles + 2, L.nc1, ntiles + 32};
     int32_t* queues = (int32_t*)(ws + L.queues);
     float* part = (float*)(ws + L.part);
     mark(0);
@@ -277,6 +278,8 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     g.n_work_gateup = wl0.count;
     g.work_down = wl1.items;
     g.n_work_down = wl1.count;
+    g.bounds_gateup = wl0.bounds;
+    g.bounds_down = wl1.bounds;
     g.act = act;
     g.y = y;
     g.decode = L.decode;

@@ -219,7 +219,13 @@ struct WorkList {
     int32_t* items;    // [max_tiles * n_col_tiles]
     int32_t* count;    // [1]
     int n_col_tiles;
+    int32_t* bounds;   // [kXcdRanges + 1]: item ranges of equal estimated cost, one per XCD
 };
+constexpr int kXcdRanges = 8;
+// Estimated cost of a (row tile, column tile) item: a fixed part (the weight
+// panel's DMA, which a short tile pays in full) plus one per live 32-row
+// group; per work list (gate/up, down).
+constexpr int kItemFixedCost[2] = {5, 5};
 // zero[0 .. n_zero-1] is cleared (the GEMMs' work-queue counters).
 hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx,
                              int32_t* blk_counts /*in: counts, out: bases*/,
@@ -248,6 +254,8 @@ struct GemmProblem {
     const int32_t* n_work_gateup;
     const int32_t* work_down;
     const int32_t* n_work_down;
+    const int32_t* bounds_gateup;  // [kXcdRanges + 1] item range of each XCD
+    const int32_t* bounds_down;
     void* act;  // [T*k, I] act_dtype (expert-major rows)
     float* y;   // [T*k, H] fp32, indexed by assignment t*k+slot
     bool decode;  // use the skinny (decode) kernels; tiles are decode_block_m() rows

@@ -48,6 +48,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     __shared__ int32_t toff[1025];
     __shared__ int32_t wsum[16];
     __shared__ int32_t wtile[16];
+    __shared__ int32_t csum[2][16];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -143,6 +144,58 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     if (tid == 0) {
         if (w0.count) w0.count[0] = toff[E] * w0.n_col_tiles;
         if (w1.count) w1.count[0] = toff[E] * w1.n_col_tiles;
+    }
+
+    // 3b. each work list cut into kXcdRanges contiguous ranges of equal
+    //     estimated cost.  Expert e's items cost nc * se (se: one column of its
+    //     tiles); the experts' cost intervals, from a block scan, partition
+    //     [0, total), and the expert whose interval holds x * total / 8 finds
+    //     the first of its items that starts at or past that cost.
+    {
+        int groups = 0;  // live 32-row groups over this expert's tiles
+        for (int j = 0; j < nt; ++j) groups += (min(BM, cnt - j * BM) + 31) / 32;
+        int se[2], ce[2], xc[2];
+#pragma unroll
+        for (int l = 0; l < 2; ++l) {
+            se[l] = kItemFixedCost[l] * nt + groups;
+            ce[l] = (l ? w1.n_col_tiles : w0.n_col_tiles) * se[l];
+            xc[l] = wave_incl_scan(ce[l], lane);
+            if (lane == 63) csum[l][wave] = xc[l];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int l = 0; l < 2; ++l) {
+            const WorkList& w = l ? w1 : w0;
+            if (!w.items || !w.bounds) continue;  // uniform
+            const int nc = w.n_col_tiles;
+            int bc = 0, tot = 0;
+            for (int ww = 0; ww < 16; ++ww) {
+                if (ww < wave) bc += csum[l][ww];
+                tot += csum[l][ww];
+            }
+            const int pe = bc + xc[l] - ce[l];
+            if (tid == 0) {
+                w.bounds[0] = 0;
+                w.bounds[kXcdRanges] = toff[E] * nc;
+                if (tot == 0)
+                    for (int x = 1; x < kXcdRanges; ++x) w.bounds[x] = 0;
+            }
+            if (ce[l] > 0) {
+                for (int x = 1; x < kXcdRanges; ++x) {
+                    const long long target = (long long)tot * x / kXcdRanges;
+                    if (target < pe || target >= (long long)pe + ce[l]) continue;
+                    const int rem0 = (int)(target - pe);
+                    const int c = rem0 / se[l];
+                    const int rem = rem0 - c * se[l];
+                    int j = 0, acc = 0;
+                    while (acc < rem) {
+                        acc += kItemFixedCost[l] + (min(BM, cnt - j * BM) + 31) / 32;
+                        ++j;
+                    }
+                    w.bounds[x] = toff[tid] * nc + c * nt + j;
+                }
+            }
+        }
     }
 
     // 4. stable scatter: row = offsets[e] + (earlier tiles' count) + rank in tile.
