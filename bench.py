@@ -88,14 +88,16 @@ def weight_bytes_touched(counts, H, I, elem_bytes):
 
 def measured_traffic():
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
-    counter summary, valid only while the kernel source is unchanged."""
+    counter summary, valid only while the kernel source and the route scan
+    (which cuts the kernel's per-XCD work ranges) are unchanged."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
-        src = os.path.join(ROOT, "sparse_mixture_experts_token_amd", "csrc", "gemm_bf16.hip")
-        digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != digest:
-            return None
+        csrc = os.path.join(ROOT, "sparse_mixture_experts_token_amd", "csrc")
+        for key, name in (("source_sha256", "gemm_bf16.hip"), ("route_scan_sha256", "route_scan.hip")):
+            digest = hashlib.sha256(open(os.path.join(csrc, name), "rb").read()).hexdigest()
+            if rec.get(key) != digest:
+                return None
         return rec.get("hbm_bytes_per_launch")
     except (OSError, ValueError):
         return None

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     //     estimated cost.  Expert e's items cost nc * se (se: one column of its
     //     tiles); the experts' cost intervals, from a block scan, partition
     //     [0, total), and the expert whose interval holds x * total / 8 finds
-    //     the first of its items that starts at or past that cost.
+    //     the first of its items that starts at or past that cost, then
+    //     moves the cut to the nearer end of that column tile's row tiles.
     {
         int groups = 0;  // live 32-row groups over this expert's tiles
         for (int j = 0; j < nt; ++j) groups += (min(BM, cnt - j * BM) + 31) / 32;
@@ -192,7 +193,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
                         acc += kItemFixedCost[l] + (min(BM, cnt - j * BM) + 31) / 32;
                         ++j;
                     }
-                    w.bounds[x] = toff[tid] * nc + c * nt + j;
+                    // snap to the nearer end of column tile c's row tiles, so
+                    // that one XCD runs all of them and its L2 serves the
+                    // weight panel's repeats
+                    w.bounds[x] = toff[tid] * nc + (2 * j <= nt ? c : c + 1) * nt;
                 }
             }
         }
