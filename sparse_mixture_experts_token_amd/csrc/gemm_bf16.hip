@@ -468,23 +468,49 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
 
     // ---- epilogue: D[v] of a 32x32 tile is row 8(v/4) + 4(l/32) + v%4, column l%32 ----
     const int fr = lane & 31, fh = lane >> 5;
+    if constexpr (MODE == 0) {
 #pragma unroll
-    for (int i = 0; i < C::MBW; ++i) {
+        for (int i = 0; i < C::MBW; ++i) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int r = (wm + kWM * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
-            if (r >= rows) continue;
-            if constexpr (MODE == 0) {
+            for (int v = 0; v < 16; ++v) {
+                const int r = (wm + kWM * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
+                if (r >= rows) continue;
                 uint16_t* orow = reinterpret_cast<uint16_t*>(args.out) + (size_t)(row0 + r) * N;
 #pragma unroll
                 for (int j = 0; j < C::NBW; ++j) {
                     const int n = n0 + (wn * C::NBW + j) * 32 + fr;
                     if (n < N) orow[n] = (uint16_t)f32_to_bf16_bits(silu_f(acc[0][i][j][v]) * acc[1][i][j][v]);
                 }
-            } else {
-                const int asg = args.perm_src[row0 + r];
-                const float p = args.topk_w[asg];
-                float* orow = reinterpret_cast<float*>(args.out) + (size_t)asg * N;
+            }
+        }
+    } else {
+        // Each row's assignment and routing weight, fetched once per tile (two
+        // dependent loads per row) into the LDS ring, idle once every wave has
+        // read its last fragments; the stores below then wait on no load.  The
+        // next item's DMA into the ring follows the barrier of the work loop.
+        int2* rtab = reinterpret_cast<int2*>(smem);
+        wait_lds_reads();
+        bare_barrier();
+        if (tid < rows) {  // rows <= kBM <= kThreads
+            const int asg = args.perm_src[row0 + tid];
+            rtab[tid] = make_int2(asg, __float_as_int(args.topk_w[asg]));
+        }
+        wait_lds_reads();
+        bare_barrier();
+#pragma unroll
+        for (int i = 0; i < C::MBW; ++i) {
+            int2 ap[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = (wm + kWM * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
+                ap[v] = rtab[max(min(r, rows - 1), 0)];
+            }
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = (wm + kWM * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
+                if (r >= rows) continue;
+                const float p = __int_as_float(ap[v].y);
+                float* orow = reinterpret_cast<float*>(args.out) + (size_t)ap[v].x * N;
 #pragma unroll
                 for (int j = 0; j < C::NBW; ++j) {
                     const int n = n0 + (wn * C::NBW + j) * 32 + fr;
