@@ -639,26 +639,23 @@ int mxfp4_max_k() {
     return (int)((kMaxLds - fixed) / rows * 32) / 64 * 64;
 }
 
-template <bool MXW, class Kern>
-hipError_t launch_mode(Kern kern, size_t smem, const BArgs& a, hipStream_t stream) {
-    static const hipError_t attr = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                       (int)kMaxLds);
+template <auto Kern>
+hipError_t launch_mode(size_t smem, const BArgs& a, hipStream_t stream) {
+    const hipError_t attr = set_max_dynamic_lds<Kern>((int)kMaxLds);
     if (attr != hipSuccess) return attr;
-    return launch(kern, smem, a, stream);
+    return launch(Kern, smem, a, stream);
 }
 
 hipError_t launch_gateup_bf16w(const GemmProblem& p, hipStream_t stream) {
     const BArgs a = make_args(p, 0);
-    if (p.expert_dtype == DT_MXFP4)
-        return launch_mode<true>(gateup_bf16_kernel<true>, CfgGateUp<true>::smem(a.K), a, stream);
-    return launch_mode<false>(gateup_bf16_kernel<false>, CfgGateUp<false>::smem(a.K), a, stream);
+    if (p.expert_dtype == DT_MXFP4) return launch_mode<gateup_bf16_kernel<true>>(CfgGateUp<true>::smem(a.K), a, stream);
+    return launch_mode<gateup_bf16_kernel<false>>(CfgGateUp<false>::smem(a.K), a, stream);
 }
 
 hipError_t launch_down_bf16w(const GemmProblem& p, hipStream_t stream) {
     const BArgs a = make_args(p, 1);
-    if (p.expert_dtype == DT_MXFP4)
-        return launch_mode<true>(down_bf16_kernel<true>, CfgDown<true>::smem(a.K), a, stream);
-    return launch_mode<false>(down_bf16_kernel<false>, CfgDown<false>::smem(a.K), a, stream);
+    if (p.expert_dtype == DT_MXFP4) return launch_mode<down_bf16_kernel<true>>(CfgDown<true>::smem(a.K), a, stream);
+    return launch_mode<down_bf16_kernel<false>>(CfgDown<false>::smem(a.K), a, stream);
 }
 
 }  // namespace moe

@@ -716,11 +716,9 @@ int cu_count() {
 
 constexpr int kMaxLds = 160 * 1024;
 
-template <typename Kern>
-hipError_t allow_lds(Kern kern) {
-    static const hipError_t attr =
-        hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLds - 1024);
-    return attr;
+template <auto Kern>
+hipError_t allow_lds() {
+    return set_max_dynamic_lds<Kern>(kMaxLds - 1024);
 }
 
 template <int MODE, int WDT, int DEPTH, int NP>
@@ -749,7 +747,7 @@ hipError_t launch_gu(const GemmProblem& p, hipStream_t stream) {
     } else {
         const DArgs a = make_dargs(p, 0);
         auto kern = decode_balanced_kernel<0, WDT, 1>;
-        const hipError_t attr = allow_lds(kern);
+        const hipError_t attr = allow_lds<decode_balanced_kernel<0, WDT, 1>>();
         if (attr != hipSuccess) return attr;
         kern<<<cu_count(), kGuWaves * 64, kMinLds, stream>>>(a);
         return hipGetLastError();
@@ -781,7 +779,7 @@ hipError_t launch_fused(const GemmProblem& p, const FusedRouting& r, hipStream_t
     const uint32_t smem = L.total > (uint32_t)kMinLds ? L.total : (uint32_t)kMinLds;
     if (smem > (uint32_t)(kMaxLds - 1024)) return hipErrorInvalidValue;
     auto kern = decode_route_gateup_kernel<WDT>;
-    const hipError_t attr = allow_lds(kern);
+    const hipError_t attr = allow_lds<decode_route_gateup_kernel<WDT>>();
     if (attr != hipSuccess) return attr;
     kern<<<cu_count(), kGuWaves * 64, smem, stream>>>(f);
     return hipGetLastError();

@@ -206,6 +206,16 @@ __device__ __forceinline__ f32x4 mfma16(float a, float b, f32x4 c) {
 // Stage 0: router logits + top-k + selected softmax + per-tile counts/ranks.
 // With part non-null the logits are the slice sums of part [kLogitSlices][T][E]
 // (launch_decode_logits) plus the bias, instead of being computed from h.
+// Raise one kernel's dynamic LDS limit, once per process.  The static lives
+// in the instantiation for that kernel (not for its type: kernels with one
+// signature share a type), so every kernel gets its own call.
+template <auto Kern>
+hipError_t set_max_dynamic_lds(int bytes) {
+    static const hipError_t attr =
+        hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    return attr;
+}
+
 hipError_t launch_router(int act_dtype, const void* h, const void* w_router, const void* b_router,
                          int T, int H, int E, int k, float* logits_opt, int32_t* topk_idx,
                          float* topk_w, int32_t* blk_counts /*[E][nblk]*/, int32_t* local_rank,

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert smoe.moe_status_string(code) and smoe.moe_status_string(code) != "unknown status"
     assert smoe.moe_status_string(-99) == "unknown status"
     assert smoe.moe_stage_name(2) == "gateup_swiglu_gemm"

@@ -321,6 +321,30 @@ def test_routing_metadata_by_explicit_walk():
 
 # ---------------------------------------------------------------- MXFP4 --
 
+def test_widen_bf16_bit_patterns():
+    """bf16 is the high half of an IEEE binary32: 1 sign bit, 8 exponent bits
+    (bias 127), 7 fraction bits.  Each stored pattern below has a value that
+    the format fixes by itself (normal, subnormal, signed zero, infinities,
+    NaN, the largest finite value), so a shift, a sign extension or a byte
+    swap in the widening fails one of them."""
+    cases = {
+        0x0000: 0.0, 0x3F80: 1.0, 0xC000: -2.0, 0xBE80: -0.25, 0x3F81: 1.0 + 2.0 ** -7,
+        0x4049: 3.140625, 0x0080: 2.0 ** -126, 0x0001: 2.0 ** -133, 0x007F: 127 * 2.0 ** -133,
+        0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127, 0xFF7F: -(2.0 - 2.0 ** -7) * 2.0 ** 127,
+        0x7F80: np.inf, 0xFF80: -np.inf,
+    }
+    bits = np.array(list(cases), dtype=np.uint16).reshape(-1, 1)
+    got = oracle.widen(bits, "bf16")
+    assert got.shape == bits.shape and got.dtype == np.float64
+    np.testing.assert_array_equal(got.ravel(), np.array(list(cases.values())))
+    neg0 = oracle.widen(np.array([0x8000], dtype=np.uint16), "bf16")[0]
+    assert neg0 == 0.0 and np.signbit(neg0)
+    assert np.isnan(oracle.widen(np.array([0x7FC0, 0xFFC1], dtype=np.uint16), "bf16")).all()
+    # fp32 storage widens without change
+    f = np.array([1.5, -2.0 ** -149, 3.4028234663852886e38], dtype=np.float32)
+    np.testing.assert_array_equal(oracle.widen(f, "f32"), [1.5, -2.0 ** -149, 3.4028234663852886e38])
+
+
 def test_e2m1_decode_matches_spec_table():
     for code, val in _rows("e2m1_table.txt"):
         got = oracle.e2m1_value(int(code))
