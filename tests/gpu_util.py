@@ -49,17 +49,34 @@ def oracle_weights(layer: synth.Layer, stacked: dict) -> oracle.LayerWeights:
                                             lambda e: {n: a[e] for n, a in stacked.items()})
 
 
-def run(prob: smoe.Problem, w: dict, h: torch.Tensor, act_fmt: str) -> dict:
-    """One forward pass with every routing output requested; results as numpy."""
+def poisoned(shape, dtype, byte: int = 0xFF, device="cuda") -> torch.Tensor:
+    """A tensor whose every byte is ``byte``: 0xFF reads as NaN in fp32 and
+    bf16 and as -1 in int32, so a result the library fails to write, or a
+    workspace region it reads before writing, shows up in the comparison."""
+    t = torch.empty(shape, dtype=dtype, device=device)
+    t.view(torch.uint8).fill_(byte)
+    return t
+
+
+def routing_outputs(T: int, E: int, k: int, dev, byte: int = 0xFF) -> dict:
+    return {"logits": poisoned((T, E), torch.float32, byte, dev),
+            "topk_idx": poisoned((T, k), torch.int32, byte, dev),
+            "topk_w": poisoned((T, k), torch.float32, byte, dev),
+            "expert_offsets": poisoned((E + 1,), torch.int32, byte, dev),
+            "perm_src": poisoned((T * k,), torch.int32, byte, dev)}
+
+
+def run(prob: smoe.Problem, w: dict, h: torch.Tensor, act_fmt: str, byte: int = 0xFF) -> dict:
+    """One forward pass with every routing output requested; results as numpy.
+    The workspace, the output and the routing outputs are filled with
+    ``byte`` first (0xFF: NaN), so stale or unwritten data cannot pass."""
     T, E, k, H = prob.T, prob.E, prob.k, prob.H
     dev = h.device
-    out = torch.empty((T, H), dtype=h.dtype, device=dev)
-    r = {"logits": torch.empty((T, E), dtype=torch.float32, device=dev),
-         "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
-         "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
-         "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-         "perm_src": torch.empty(T * k, dtype=torch.int32, device=dev)}
-    smoe.moe_forward(prob, w, h, out, routing=r)
+    out = poisoned((T, H), h.dtype, byte, dev)
+    r = routing_outputs(T, E, k, dev, byte)
+    nb = smoe.moe_workspace_bytes(prob)
+    ws = poisoned((max(nb, 1),), torch.uint8, byte, dev)
+    smoe.moe_forward(prob, w, h, out, routing=r, workspace=ws, workspace_bytes=nb)
     torch.cuda.synchronize()
     res = {n: t.cpu().numpy() for n, t in r.items()}
     res["out"] = out.float().cpu().numpy().astype(np.float64)
@@ -104,6 +121,23 @@ def check_out(got: np.ndarray, ref: np.ndarray, fmt: str) -> dict:
     return {"rel_l2": r, "max_abs": mx, "max_ref": lim}
 
 
+_ref_cache: dict = {}
+
+
+def reference_out(layer: synth.Layer, stacked: dict, T: int, idx: np.ndarray, tokens=None) -> np.ndarray:
+    """fp64 outputs of the first ``T`` tokens of a workload with selection
+    ``idx`` (cached: the full-size layers take tens of seconds)."""
+    c = layer.cfg
+    key = (c, T, hash(idx.tobytes()), None if tokens is None else hash(np.asarray(tokens).tobytes()))
+    if key not in _ref_cache:
+        if len(_ref_cache) > 4:
+            _ref_cache.clear()
+        ow = oracle_weights(layer, stacked)
+        h64 = oracle.widen(layer.h[:T], c.act)
+        _ref_cache[key] = oracle.moe_forward(h64, ow, c.k, idx=idx, tokens=tokens, workers=workers())["out"]
+    return _ref_cache[key]
+
+
 def check_layer(layer: synth.Layer, stacked: dict, w_dev: dict | None = None, tokens=None, T: int | None = None):
     """Full parity check of one layer: routing bit-exact (after near-ties),
     outputs within tolerance on ``tokens`` (default all)."""
@@ -127,8 +161,8 @@ def check_layer(layer: synth.Layer, stacked: dict, w_dev: dict | None = None, to
     np.testing.assert_allclose(g["logits"], s, rtol=0, atol=1e-5 * max(1.0, np.abs(s).max()))
     p_ref = oracle.selected_softmax(s, eff)
     np.testing.assert_allclose(g["topk_w"], p_ref, rtol=0, atol=2e-6)
-    ref = oracle.moe_forward(h64, ow, c.k, idx=eff, tokens=tokens, workers=workers())
+    ref_out = reference_out(layer, stacked, T, eff, tokens)
     got = g["out"] if tokens is None else g["out"][tokens]
-    m = check_out(got, ref["out"], c.act)
+    m = check_out(got, ref_out, c.act)
     m.update(n_near=n_near, n_swapped=n_swapped)
     return m, g

@@ -14,23 +14,23 @@ import torch
 import oracle
 import sparse_mixture_experts_token_amd as smoe
 import synth
-from gpu_util import check_out, device_weights, oracle_weights, problem, reconcile, to_dev, workers
+from gpu_util import (check_out, device_weights, oracle_weights, poisoned, problem, reconcile, routing_outputs, to_dev,
+                      workers)
 
 pytestmark = pytest.mark.gpu
 
 EPS = 1e-5
 
 
-def run_block(prob, w, g, x, eps=EPS):
+def run_block(prob, w, g, x, eps=EPS, byte=0xFF):
+    """Workspace, output and routing outputs filled with ``byte`` (0xFF: NaN) first."""
     T, E, k, H = prob.T, prob.E, prob.k, prob.H
     dev = x.device
-    out = torch.empty((T, H), dtype=x.dtype, device=dev)
-    r = {"logits": torch.empty((T, E), dtype=torch.float32, device=dev),
-         "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
-         "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
-         "expert_offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-         "perm_src": torch.empty(T * k, dtype=torch.int32, device=dev)}
-    smoe.moe_block_forward(prob, w, g, eps, x, out, routing=r)
+    out = poisoned((T, H), x.dtype, byte, dev)
+    r = routing_outputs(T, E, k, dev, byte)
+    nb = smoe.moe_block_workspace_bytes(prob)
+    ws = poisoned((max(nb, 1),), torch.uint8, byte, dev)
+    smoe.moe_block_forward(prob, w, g, eps, x, out, routing=r, workspace=ws, workspace_bytes=nb)
     torch.cuda.synchronize()
     res = {n: t.cpu().numpy() for n, t in r.items()}
     res["out"] = out.float().cpu().numpy().astype(np.float64)
@@ -63,8 +63,9 @@ def check_block(L, st, T):
     return m, got
 
 
-@pytest.mark.parametrize("key,T", [(2, 256), (2, 64), (1, 64)],
-                         ids=["gpt-oss-20b-T256-prefill-kernels", "gpt-oss-20b-T64-decode-kernels", "fixture-fp32"])
+@pytest.mark.parametrize("key,T", [(2, 4096), (2, 256), (2, 64), (1, 64)],
+                         ids=["gpt-oss-20b-T4096-prefill", "gpt-oss-20b-T256-prefill-kernels",
+                              "gpt-oss-20b-T64-decode-kernels", "fixture-fp32"])
 def test_block_parity(key, T):
     L = synth.make_layer(key)
     m, _ = check_block(L, L.stacked(), T)
@@ -101,7 +102,7 @@ def test_block_deterministic():
     c = L.cfg
     x, g = synth.block_inputs(L)
     w = device_weights(L, st)
-    a = run_block(problem(c, L.T), w, to_dev(g, c.act), to_dev(x, c.act))
-    b = run_block(problem(c, L.T), w, to_dev(g, c.act), to_dev(x, c.act))
+    a = run_block(problem(c, L.T), w, to_dev(g, c.act), to_dev(x, c.act), byte=0xFF)
+    b = run_block(problem(c, L.T), w, to_dev(g, c.act), to_dev(x, c.act), byte=0x7F)
     assert torch.equal(a["out_raw"], b["out_raw"])
     np.testing.assert_array_equal(a["logits"], b["logits"])
