@@ -62,7 +62,8 @@ enum {
     MOE_ERR_ALIGN     = -5, /* a pointer is not 16-byte aligned                  */
     MOE_ERR_HIP       = -6, /* the HIP runtime reported an error at enqueue      */
     MOE_ERR_STATE     = -7, /* profiling calls out of order                      */
-    MOE_ERR_DISABLED  = -8  /* entry point switched off in this build (see it)   */
+    MOE_ERR_DISABLED  = -8, /* entry point switched off in this build (see it)   */
+    MOE_ERR_SCRATCH   = -9  /* problem larger than moe_forward_noalloc's scratch */
 };
 
 /* Problem sizes; field names follow the model configs on the pages
@@ -139,6 +140,25 @@ size_t moe_workspace_bytes(const moe_problem *p);
 int moe_forward(const moe_problem *p, const moe_weights *w, const void *h, void *out,
                 const moe_routing *routing, void *workspace, size_t workspace_bytes,
                 void *stream);
+
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, arithmetic, results and errors as moe_forward, without the
+ * workspace: its regions live in one static device array of the library,
+ * MOE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which each GPU the library runs
+ * on holds from its first call until the process ends.  A problem whose
+ * moe_workspace_bytes() exceeds that (e.g. T = 4096 prefill of the
+ * gpt-oss-20b layer) gets MOE_ERR_SCRATCH and nothing is enqueued; decode
+ * batches and short prefill chunks fit (the gpt-oss-20b layer up to T of
+ * about 900).  The call allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine.  Every call on one GPU shares that GPU's array,
+ * and the array keeps the previous call's contents (the kernels clear what
+ * must start at zero themselves), so calls that overlap on one GPU (two
+ * streams, or two threads) race and must be serialised by the caller.
+ * `stream` must belong to the current device (else MOE_ERR_HIP). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const moe_problem *p, const moe_weights *w, const void *h, void *out,
+                        const moe_routing *routing, void *stream);
 
 /* The pre-normalised MoE sublayer of a decoder block with its residual add
  * ("gpt-oss 20B" field guide, cutaway 04 "One decoder block": RMSNorm before

@@ -10,6 +10,7 @@ The functions mirror the C entry points of ``include/moe.h``:
 
 * ``moe_workspace_bytes(problem)``
 * ``moe_forward(problem, weights, h, out, routing=None, workspace=None)``
+* ``moe_forward_noalloc(problem, weights, h, out, routing=None)``
 * ``moe_block_workspace_bytes(problem)``
 * ``moe_block_forward(problem, weights, norm_weight, eps, x, out, routing=None, workspace=None)``
 * ``moe_backward_workspace_bytes(problem)``
@@ -40,8 +41,9 @@ MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
 MOE_NUM_STAGES = 5
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
           -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_HIP", -7: "MOE_ERR_STATE",
-          -8: "MOE_ERR_DISABLED"}
-EXPORTED = ("moe_workspace_bytes", "moe_forward", "moe_block_workspace_bytes", "moe_block_forward",
+          -8: "MOE_ERR_DISABLED", -9: "MOE_ERR_SCRATCH"}
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+EXPORTED = ("moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_block_workspace_bytes", "moe_block_forward",
             "moe_backward_workspace_bytes", "moe_backward", "moe_attn_workspace_bytes", "moe_attn_sink_decode", "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
             "moe_profile_begin", "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name")
 MOE_PROFILE_ALL = (1 << (MOE_NUM_STAGES + 1)) - 1
@@ -129,6 +131,9 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_void_p, ctypes.c_void_p,
                                 ctypes.POINTER(_Routing), ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.POINTER(_Routing), ctypes.c_void_p]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_block_workspace_bytes.argtypes = [ctypes.POINTER(_Problem)]
     lib.moe_block_workspace_bytes.restype = ctypes.c_size_t
     lib.moe_block_forward.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_void_p,
@@ -241,6 +246,19 @@ def moe_forward(problem: Problem, weights: dict, h, out, routing: dict | None = 
                          ctypes.byref(r) if r is not None else None, _ptr(workspace), int(workspace_bytes),
                          _stream(stream))
     _check(st)
+
+
+def moe_forward_noalloc(problem: Problem, weights: dict, h, out, routing: dict | None = None, stream=None) -> None:
+    """``moe_forward`` on the library's static per-GPU scratch (no workspace,
+    nothing allocated by the call); problems needing more than
+    ``MOE_NOALLOC_SCRATCH_BYTES`` of workspace raise MOE_ERR_SCRATCH.  Calls
+    that overlap on one GPU share the scratch and race."""
+    lib = load()
+    p = problem._c()
+    w = _weights(weights)
+    r = _routing(routing)
+    _check(lib.moe_forward_noalloc(ctypes.byref(p), ctypes.byref(w), _ptr(h), _ptr(out),
+                                   ctypes.byref(r) if r is not None else None, _stream(stream)))
 
 
 def moe_block_workspace_bytes(problem: Problem) -> int:

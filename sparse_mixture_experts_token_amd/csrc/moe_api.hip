@@ -8,9 +8,38 @@
 #include "moe.h"
 #include "moe_internal.h"
 
+// Scratch of moe_forward_noalloc: the workspace regions of one call, in a
+// static array that each device holds from the code object's load on.  Host
+// code never uses this name as an address (it is only a host-side stand-in);
+// kernels get the device address from hipGetSymbolAddress below.
+__device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 using moe::Tile;
+
+// Per-device address of `scratch`, looked up once per device with that device
+// current (each device holds its own copy of the array at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(hipStream_t stream, char** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    if (stream) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return MOE_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = static_cast<char*>(ptr);
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
 
 constexpr size_t kAlign = 256;
 
@@ -320,6 +349,7 @@ const char* moe_status_string(int s) {
         case MOE_ERR_HIP: return "HIP runtime error at enqueue";
         case MOE_ERR_STATE: return "profiling calls out of order";
         case MOE_ERR_DISABLED: return "entry point switched off in this build (moe_backward: GPU fault under investigation)";
+        case MOE_ERR_SCRATCH: return "problem needs more workspace than moe_forward_noalloc's static scratch (MOE_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -345,6 +375,27 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     in.gemm_h = h;
     return run_pass(p, w, in, out, routing, reinterpret_cast<char*>(workspace), L,
                     reinterpret_cast<hipStream_t>(stream_v));
+}
+
+int moe_forward_noalloc(const moe_problem* p, const moe_weights* w, const void* h, void* out,
+                        const moe_routing* routing, void* stream_v) {
+    bool noop = false;
+    // the static scratch is 256-byte aligned: pass any aligned non-null stand-in to the shared checks
+    int st = check_call(p, w, h, out, routing, reinterpret_cast<const void*>(kAlign), &noop);
+    if (st != MOE_OK || noop) return st;
+    const Layout L = layout(p);
+    if (L.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
+    char* ws = nullptr;
+    st = scratch_of_current_device(stream, &ws);
+    if (st != MOE_OK) return st;
+    PassIn in{};
+    in.router_dt = p->act_dtype;
+    in.router_h = h;
+    in.w_router = w->w_router;
+    in.b_router = w->b_router;
+    in.gemm_h = h;
+    return run_pass(p, w, in, out, routing, ws, L, stream);
 }
 
 size_t moe_block_workspace_bytes(const moe_problem* p) {

@@ -20,14 +20,14 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = smoe.load()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(smoe.EXPORTED) == names
 
 
 def test_status_strings():
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert smoe.moe_status_string(code) and smoe.moe_status_string(code) != "unknown status"
     assert smoe.moe_status_string(-99) == "unknown status"
     assert smoe.moe_stage_name(2) == "gateup_swiglu_gemm"
@@ -184,3 +184,26 @@ def test_profile_mask_argument_errors():
     assert lib.moe_profile_begin_mask(4, 0) == -2                                  # empty mask
     assert lib.moe_profile_begin_mask(4, smoe.MOE_PROFILE_ALL + 1) == -2          # bit beyond the last boundary
     assert lib.moe_profile_begin_mask(0, smoe.MOE_PROFILE_ALL) == -2              # no calls
+
+
+def test_noalloc_argument_errors_return_before_any_launch():
+    """moe_forward_noalloc checks its arguments, and the problem's workspace
+    against the static scratch limit, before it touches the device."""
+    lib = smoe.load()
+
+    def call(p, h=0x1000, out=0x2000, weights=None):
+        w = smoe._Weights(*[weights.get(n) if weights else 0x4000 for n in smoe._WEIGHT_FIELDS])
+        return lib.moe_forward_noalloc(ctypes.byref(p._c()) if p is not None else None, ctypes.byref(w), h, out,
+                                       None, None)
+
+    P = smoe.Problem(16, 64, 128, 4, 2, smoe.MOE_BF16, smoe.MOE_BF16)
+    assert call(None) == -1
+    assert call(P, h=0) == -1 and call(P, out=0) == -1
+    assert call(P, h=0x1004) == -5
+    assert call(smoe.Problem(16, 64, 128, 4, 5)) == -2
+    assert call(smoe.Problem(16, 64, 128, 4, 2, smoe.MOE_F32, smoe.MOE_BF16)) == -3
+    big = smoe.Problem(4096, 2880, 2880, 32, 4)   # the gpt-oss-20b layer at prefill: ~285 MB of workspace
+    assert smoe.moe_workspace_bytes(big) > smoe.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(big) == -9
+    assert "scratch" in smoe.moe_status_string(-9)
+    assert call(smoe.Problem(0, 64, 128, 4, 2), h=0, out=0) == 0
