@@ -41,7 +41,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gateup_gemm_c2_prefill_traffic.js
 
 # The other layers the method is quoted on: (synth config key, tokens, silent
 # expansion factor of the gpt-oss-20b layer, 0 for none or -1 for the
-# pre-normalised block around the layer, description).
+# pre-normalised block around the layer, or the new expert count of an
+# expansion by copy map, description).  Expanded layers run at k' = M*k unless
+# NARROW_K names the top-k they are deployed with.
 OTHER_WORKLOADS = {
     "c3-64a8": (3, 4096, 0, "random 64-expert top-8 layer (64a8 shape), prefill T=4096, bf16"),
     "c3-96a12": (2, 4096, 3, "gpt-oss-20b layer silently expanded x3 (96a12), top-12, prefill T=4096, bf16"),
@@ -49,12 +51,20 @@ OTHER_WORKLOADS = {
                        "assignments, prefill T=8192"),
     "c5": (5, 2048, 0, "220a20b-shaped layer (248 experts, top-20), MXFP4 experts, prefill T=2048"),
     "c5-decode": (5, 32, 0, "220a20b-shaped layer (248 experts, top-20), MXFP4 experts, decode T=32"),
+    "c3-64a4": (2, 4096, 2, "deploy-narrow 64a4: gpt-oss-20b layer silently expanded x2 (64 experts), run at top-4, "
+                            "prefill T=4096, bf16"),
+    "c3-96a4": (2, 4096, 3, "deploy-narrow 96a4: gpt-oss-20b layer silently expanded x3 (96 experts), run at top-4, "
+                            "prefill T=4096, bf16"),
+    "c4-248a20": (4, 2048, 248, "248 expert rows (128 base + 120 added, added row 128+j a copy of base row j) built "
+                                "from the 120b-shaped MXFP4 layer, top-20, prefill T=2048"),
     "block-c2": (2, 4096, -1, "pre-normalised block x + MoE(RMSNorm(x)) on the gpt-oss-20b layer, prefill T=4096, "
                               "bf16, eps 1e-5"),
     "block-c2-decode": (2, 64, -1, "pre-normalised block x + MoE(RMSNorm(x)) on the gpt-oss-20b layer, decode T=64, "
                                    "bf16, eps 1e-5"),
 }
 BLOCK_EPS = 1e-5
+NARROW_K = {"c3-64a4": 4, "c3-96a4": 4, "c4-248a20": 20}
+COPY_MAP = {"c4-248a20": list(range(128)) + list(range(120))}
 
 
 def parse():
@@ -222,12 +232,20 @@ def other_workloads(names, args):
         L, w = layers[key]
         c = L.cfg
         E, k = c.E, c.k
-        if M > 1:  # silent expansion on the device: every expert tensor repeated M times
+        if name in COPY_MAP:  # expansion by a copy map on the device
+            cmap = COPY_MAP[name]
+            base = smoe.Problem(0, c.H, c.I, E, k, DT[c.act], DT[c.expert])
+            w = {n: torch.empty((len(cmap),) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
+                 for n, t in layers[key][1].items()}
+            smoe.moe_expand_copies(base, layers[key][1], cmap, w)
+            E = len(cmap)
+        elif M > 1:  # silent expansion on the device: every expert tensor repeated M times
             base = smoe.Problem(0, c.H, c.I, E, k, DT[c.act], DT[c.expert])
             w = {n: torch.empty((M * t.shape[0],) + tuple(t.shape[1:]), dtype=t.dtype, device=dev)
                  for n, t in layers[key][1].items()}
             smoe.moe_expand_silent(base, layers[key][1], M, w)
             E, k = M * E, M * k
+        k = NARROW_K.get(name, k)
         prob = smoe.Problem(T, c.H, c.I, E, k, DT[c.act], DT[c.expert])
         offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
         if M < 0:  # the pre-normalised block: x = h with rows rescaled, gain g

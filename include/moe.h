@@ -267,6 +267,23 @@ int moe_backward(const moe_problem *p, const moe_weights *w, const void *h, cons
 int moe_expand_silent(const moe_problem *base, const moe_weights *src, int32_t M,
                       const moe_weights *dst, void *stream);
 
+/* Expansion by an explicit copy map, for expansions that do not repeat every
+ * expert the same number of times (the "gpt-oss-220a20b" page, Model Details:
+ * 248 expert rows made of 128 base rows and 120 added rows): for every
+ * per-expert tensor of *src (as in moe_expand_silent) write dst row j =
+ * src row copy_of[j], j = 0 .. E_new-1.  copy_of is a HOST array of E_new
+ * int32 original expert ids in 0 .. base->E-1; each new row starts as an
+ * exact copy of its original, router row and bias included, so copies of one
+ * original get bitwise-equal logits and exact ties between them go to the
+ * lower expanded id.  The caller runs the expanded layer with E' = E_new and
+ * its chosen k'.  moe_expand_silent(M) is copy_of[j] = j mod E.  Runs of rows
+ * that copy consecutive originals go out as one device copy each.
+ * Errors: MOE_ERR_NULL (base, src, dst, copy_of, or a required tensor),
+ * MOE_ERR_SHAPE (E_new outside 1..1024, an id outside 0..E-1, invalid base),
+ * MOE_ERR_DTYPE, MOE_ERR_HIP. */
+int moe_expand_copies(const moe_problem *base, const moe_weights *src, const int32_t *copy_of, int32_t E_new,
+                      const moe_weights *dst, void *stream);
+
 /* Decode MXFP4 weights to bf16 with the same device routine the forward pass
  * uses when it stages weight tiles.  `packed` holds n_groups runs of 16 bytes
  * (32 E2M1 codes, element 2j in the low nibble of byte j), `scales` one E8M0

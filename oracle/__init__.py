@@ -47,6 +47,7 @@ from .moe import (
     moe_forward_per_token,
     routing_metadata,
     expand_silent,
+    expand_rows,
     LayerWeights,
 )
 from .block import rms_norm, block_forward, block_forward_per_token
@@ -57,7 +58,7 @@ __all__ = [
     "e2m1_value", "e8m0_value", "mxfp4_dequant", "mxfp4_bits_per_param",
     "widen", "router_logits", "select_topk", "topk_gap", "selected_softmax",
     "silu", "swiglu_expert", "moe_forward", "moe_forward_per_token",
-    "routing_metadata", "expand_silent", "LayerWeights",
+    "routing_metadata", "expand_silent", "expand_rows", "LayerWeights",
     "rms_norm", "block_forward", "block_forward_per_token",
     "sink_softmax", "attn_sink_decode",
     "silu_grad", "moe_backward",

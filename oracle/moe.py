@@ -249,6 +249,22 @@ def routing_metadata(idx: np.ndarray, E: int) -> dict:
 
 # ------------------------------------------------------ silent expansion --
 
+def expand_rows(x: np.ndarray, copy_of) -> np.ndarray:
+    """Expanded per-expert tensor (expert axis first) in which expanded expert
+    ``j`` is a copy of original expert ``copy_of[j]``: the silent-init
+    construction ("gpt-oss-40b-64a8-init" page, section 2: every new expert is
+    initialised from an existing one, router row included) with any number of
+    copies per original, e.g. the 248 expert rows of "gpt-oss-220a20b" (Model
+    Details: 128 base rows plus 120 added rows)."""
+    x = np.asarray(x)
+    copy_of = np.asarray(copy_of)
+    if copy_of.ndim != 1 or copy_of.size == 0:
+        raise ValueError("copy_of must be a non-empty list of original expert ids")
+    if copy_of.min() < 0 or copy_of.max() >= x.shape[0]:
+        raise ValueError("copy_of names an expert that does not exist")
+    return x[copy_of]
+
+
 def expand_silent(x: np.ndarray, M: int, copy_of: np.ndarray | None = None) -> np.ndarray:
     """Expand a per-expert tensor (expert axis first) to ``M*E`` experts.
 

@@ -18,6 +18,7 @@ The functions mirror the C entry points of ``include/moe.h``:
 * ``moe_attn_workspace_bytes(problem)``
 * ``moe_attn_sink_decode(problem, q, k_cache, v_cache, sinks, lens, out, workspace=None)``
 * ``moe_expand_silent(base, src, M, dst)``
+* ``moe_expand_copies(base, src, copy_of, dst)``
 * ``moe_status_string(status)``
 * ``moe_profile_begin(max_calls)`` / ``moe_profile_begin_mask(max_calls, mask)`` / ``moe_profile_end()``
 
@@ -44,7 +45,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTY
           -8: "MOE_ERR_DISABLED", -9: "MOE_ERR_SCRATCH"}
 MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 EXPORTED = ("moe_workspace_bytes", "moe_forward", "moe_forward_noalloc", "moe_block_workspace_bytes", "moe_block_forward",
-            "moe_backward_workspace_bytes", "moe_backward", "moe_attn_workspace_bytes", "moe_attn_sink_decode", "moe_expand_silent", "moe_mxfp4_decode", "moe_status_string",
+            "moe_backward_workspace_bytes", "moe_backward", "moe_attn_workspace_bytes", "moe_attn_sink_decode", "moe_expand_silent", "moe_expand_copies", "moe_mxfp4_decode", "moe_status_string",
             "moe_profile_begin", "moe_profile_begin_mask", "moe_profile_end", "moe_stage_name")
 MOE_PROFILE_ALL = (1 << (MOE_NUM_STAGES + 1)) - 1
 
@@ -154,6 +155,10 @@ def load() -> ctypes.CDLL:
     lib.moe_expand_silent.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights), ctypes.c_int32,
                                       ctypes.POINTER(_Weights), ctypes.c_void_p]
     lib.moe_expand_silent.restype = ctypes.c_int
+    lib.moe_expand_copies.argtypes = [ctypes.POINTER(_Problem), ctypes.POINTER(_Weights),
+                                      ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.POINTER(_Weights),
+                                      ctypes.c_void_p]
+    lib.moe_expand_copies.restype = ctypes.c_int
     lib.moe_mxfp4_decode.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
                                      ctypes.c_void_p]
     lib.moe_mxfp4_decode.restype = ctypes.c_int
@@ -329,6 +334,16 @@ def moe_attn_sink_decode(problem: AttnProblem, q, k_cache, v_cache, sinks, lens,
 def moe_expand_silent(base: Problem, src: dict, M: int, dst: dict, stream=None) -> None:
     p = base._c()
     _check(load().moe_expand_silent(ctypes.byref(p), ctypes.byref(_weights(src)), int(M),
+                                    ctypes.byref(_weights(dst)), _stream(stream)))
+
+
+def moe_expand_copies(base: Problem, src: dict, copy_of, dst: dict, stream=None) -> None:
+    """dst row j = src row copy_of[j] for every per-expert tensor; ``copy_of``
+    is a host sequence of original expert ids (its length is the new E)."""
+    ids = [int(x) for x in copy_of]
+    arr = (ctypes.c_int32 * max(len(ids), 1))(*ids)
+    p = base._c()
+    _check(load().moe_expand_copies(ctypes.byref(p), ctypes.byref(_weights(src)), arr, len(ids),
                                     ctypes.byref(_weights(dst)), _stream(stream)))
 
 

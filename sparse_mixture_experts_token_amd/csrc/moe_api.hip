@@ -524,16 +524,18 @@ int moe_attn_sink_decode(const moe_attn_problem* p, const void* q, const void* k
     return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-int moe_expand_silent(const moe_problem* base, const moe_weights* src, int32_t M, const moe_weights* dst,
-                      void* stream_v) {
-    if (!base || !src || !dst) return MOE_ERR_NULL;
+int moe_expand_copies(const moe_problem* base, const moe_weights* src, const int32_t* copy_of, int32_t E_new,
+                      const moe_weights* dst, void* stream_v) {
+    if (!base || !src || !dst || !copy_of) return MOE_ERR_NULL;
     moe_problem q = *base;
     q.T = 0;
     int st = check_problem(&q);
     if (st != MOE_OK) return st;
-    if (M < 1 || (int64_t)M * base->E > 1024) return MOE_ERR_SHAPE;
+    if (E_new < 1 || E_new > 1024) return MOE_ERR_SHAPE;
+    for (int j = 0; j < E_new; ++j)
+        if (copy_of[j] < 0 || copy_of[j] >= base->E) return MOE_ERR_SHAPE;
     const bool mx = base->expert_dtype == MOE_MXFP4;
-    const size_t E = base->E, H = base->H, I = base->I;
+    const size_t H = base->H, I = base->I;
     const size_t ab = act_bytes(base->act_dtype);
     const size_t eb = base->expert_dtype == MOE_F32 ? 4 : 2;
 
@@ -562,14 +564,27 @@ int moe_expand_silent(const moe_problem* base, const moe_weights* src, int32_t M
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_v);
     for (const T_& t : list) {
         if (!t.s) continue;
-        const size_t bytes = E * t.row_bytes;
-        for (int m = 0; m < M; ++m) {
-            if (hipMemcpyAsync(static_cast<char*>(t.d) + (size_t)m * bytes, t.s, bytes, hipMemcpyDeviceToDevice,
-                               stream) != hipSuccess)
+        // runs j0 .. j0+n-1 that copy consecutive originals: one device copy each
+        for (int j0 = 0; j0 < E_new;) {
+            int n = 1;
+            while (j0 + n < E_new && copy_of[j0 + n] == copy_of[j0] + n) ++n;
+            if (hipMemcpyAsync(static_cast<char*>(t.d) + (size_t)j0 * t.row_bytes,
+                               static_cast<const char*>(t.s) + (size_t)copy_of[j0] * t.row_bytes,
+                               (size_t)n * t.row_bytes, hipMemcpyDeviceToDevice, stream) != hipSuccess)
                 return MOE_ERR_HIP;
+            j0 += n;
         }
     }
     return MOE_OK;
+}
+
+int moe_expand_silent(const moe_problem* base, const moe_weights* src, int32_t M, const moe_weights* dst,
+                      void* stream_v) {
+    if (!base || !src || !dst) return MOE_ERR_NULL;
+    if (M < 1 || base->E < 1 || (int64_t)M * base->E > 1024) return MOE_ERR_SHAPE;
+    std::vector<int32_t> copy_of((size_t)M * base->E);
+    for (size_t j = 0; j < copy_of.size(); ++j) copy_of[j] = (int32_t)(j % (size_t)base->E);
+    return moe_expand_copies(base, src, copy_of.data(), (int32_t)copy_of.size(), dst, stream_v);
 }
 
 int moe_profile_begin(int32_t max_calls) { return moe_profile_begin_mask(max_calls, MOE_PROFILE_ALL); }

@@ -20,7 +20,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = smoe.load()
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(smoe.EXPORTED) == names
@@ -167,6 +167,15 @@ def test_expand_and_decode_argument_errors():
     w0 = smoe._Weights(*([0] * 8))
     assert lib.moe_expand_silent(ctypes.byref(P), ctypes.byref(w0), 2, ctypes.byref(w), None) == -1
     assert lib.moe_expand_silent(None, ctypes.byref(w), 2, ctypes.byref(w), None) == -1
+    ids = (ctypes.c_int32 * 3)(0, 3, 1)
+    assert lib.moe_expand_copies(ctypes.byref(P), ctypes.byref(w), None, 3, ctypes.byref(w), None) == -1
+    assert lib.moe_expand_copies(ctypes.byref(P), ctypes.byref(w), ids, 0, ctypes.byref(w), None) == -2
+    assert lib.moe_expand_copies(ctypes.byref(P), ctypes.byref(w), ids, 1025, ctypes.byref(w), None) == -2
+    bad = (ctypes.c_int32 * 3)(0, 4, 1)   # expert 4 of a 4-expert layer
+    assert lib.moe_expand_copies(ctypes.byref(P), ctypes.byref(w), bad, 3, ctypes.byref(w), None) == -2
+    neg = (ctypes.c_int32 * 3)(0, -1, 1)
+    assert lib.moe_expand_copies(ctypes.byref(P), ctypes.byref(w), neg, 3, ctypes.byref(w), None) == -2
+    assert lib.moe_expand_copies(ctypes.byref(P), ctypes.byref(w0), ids, 3, ctypes.byref(w), None) == -1
     assert lib.moe_mxfp4_decode(0x1000, 0x2000, -1, 0x3000, None) == -2
     assert lib.moe_mxfp4_decode(0, 0x2000, 4, 0x3000, None) == -1
     assert lib.moe_mxfp4_decode(0x1008, 0x2000, 4, 0x3000, None) == -5

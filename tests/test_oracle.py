@@ -287,6 +287,67 @@ def test_silent_identity_fixture_weights():
         np.testing.assert_allclose(big["out"], base["out"], rtol=1e-12, atol=1e-16)
 
 
+def _greedy_copy_counts(s_row, copies, kp):
+    """How many copies of each original a top-kp pick over the expanded logits
+    takes: originals in descending logit order (lower id first on equal
+    logits), each contributing all its copies until kp are taken.  Copies of
+    one original have equal logits, and every copy of a better original beats
+    every copy of a worse one, so the pick is exactly this fill."""
+    n = np.zeros(len(s_row), dtype=np.int64)
+    left = kp
+    for i in sorted(range(len(s_row)), key=lambda e: (-s_row[e], e)):
+        n[i] = min(copies[i], left)
+        left -= n[i]
+        if left == 0:
+            break
+    return n
+
+
+@pytest.mark.parametrize("kp", [1, 3, 4, 6, 10])
+def test_nonuniform_expansion_closed_form(kp):
+    """A non-uniform silent expansion ("gpt-oss-220a20b" Model Details: base
+    rows plus added rows; here 8 originals and 5 added rows copying originals
+    5, 2, 7, 2, 0, so originals have one to three copies): if original i
+    contributes n_i selected copies, the layer is
+    sum_i n_i e^(s_i) y_i / sum_i n_i e^(s_i), evaluated per token from the
+    base logits and base experts only."""
+    rng = np.random.default_rng(52 + kp)
+    E = 8
+    h, w, ex = rand_layer(rng, T=50, H=24, I=40, E=E)
+    cmap = np.concatenate([np.arange(E), [5, 2, 7, 2, 0]])
+    copies = np.bincount(cmap, minlength=E)
+    wx = oracle.LayerWeights(oracle.expand_rows(w.w_router, cmap), oracle.expand_rows(w.b_router, cmap),
+                             lambda j: ex[cmap[j]])
+    big = oracle.moe_forward(h, wx, kp)
+    s = h @ w.w_router.T + w.b_router
+    for t in range(len(h)):
+        n = _greedy_copy_counts(s[t], copies, kp)
+        # the selected expanded ids: for each original its n_i lowest copies
+        want_idx = sorted(j for i in range(E) for j in np.nonzero(cmap == i)[0][:n[i]])
+        np.testing.assert_array_equal(big["idx"][t], want_idx)
+        num = np.zeros(w.w_router.shape[1])
+        den = 0.0
+        for i in np.nonzero(n)[0]:
+            wg, wu, wd = ex[i]
+            g, u = wg @ h[t], wu @ h[t]
+            e = n[i] * np.exp(s[t, i] - s[t].max())
+            num += e * (wd @ (g / (1 + np.exp(-g)) * u))
+            den += e
+        np.testing.assert_allclose(big["out"][t], num / den, rtol=1e-12, atol=1e-15)
+
+
+def test_expand_rows_copies_and_checks():
+    x = np.arange(4 * 3).reshape(4, 3)
+    cmap = np.array([0, 1, 2, 3, 3, 0, 1])
+    y = oracle.expand_rows(x, cmap)
+    assert y.shape == (7, 3)
+    for j, i in enumerate(cmap):
+        np.testing.assert_array_equal(y[j], x[i])
+    for bad in ([], [4], [-1], [[0, 1]]):
+        with pytest.raises(ValueError):
+            oracle.expand_rows(x, np.array(bad, dtype=np.int64))
+
+
 def test_expansion_mapping_keeps_originals_first():
     x = np.arange(4 * 3).reshape(4, 3)
     y = oracle.expand_silent(x, 3)
