@@ -36,12 +36,14 @@
 // MXFP4 weights ("gpt-oss-20b and gpt-oss-120b" explainer, "Four-bit expert
 // weights"; element and scale encodings of OCP MX v1.0) travel packed: a
 // stage holds each weight row's 32 bytes of codes for its 64 K in 32-row 1 KB
-// blocks (lane l of a DMA fetches row l/2, half l%2).  That pattern is four
-// times slower per byte than whole-line fetches but carries a quarter of the
-// bytes, and the smaller stages leave room for a three-stage ring beside the
-// tile's E8M0 scales for all of K.  A fragment is 4 bytes of codes plus its
-// scale, decoded exactly to bf16 right before its MFMA (hardware scaled
-// conversion for scales 2..252, integer path for the extremes).
+// blocks.  That pattern is four times slower per byte than whole-line fetches
+// but carries a quarter of the bytes, and the smaller stages leave room for a
+// three-stage ring beside the tile's E8M0 scales for all of K.  The stage's K
+// order is permuted (the same for both operands) so that a lane's codes for
+// all four steps are 16 contiguous bytes under one scale: one LDS read of
+// codes and one of the scale per weight group and stage, decoded exactly to
+// bf16 right before each MFMA (hardware scaled conversion for scales 2..252,
+// integer path for the extremes).
 //
 // Block order: persistent workgroups, one per CU.  Each XCD (blocks are dealt
 // round-robin to 8) drains a contiguous range of a work list built with the
@@ -141,33 +143,47 @@ struct Cfg {
     static_assert(NMAT * MBW * NBW * 16 <= 256, "accumulators");
 };
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-
-// Weight operand of one fragment: bf16 values, or for MXFP4 the raw 8 codes
-// and their scale (decoded right before the MFMA, which halves the registers
-// the read-ahead needs).
-template <bool MX>
-struct WFrag {
-    bf16x8 v;
-};
-template <>
-struct WFrag<true> {
-    u32x2 v;  // codes, scale
-};
-
-// Fragments of two consecutive K steps for this wave's MB row groups.
-template <class C, int MB>
+// Fragments of two consecutive K steps for this wave's MB row groups.  With
+// MXFP4 weights the weight operand is held as raw codes and decoded right
+// before each MFMA (holding decoded fragments would double the registers the
+// read-ahead needs): per 32-row weight group, the lane's 16 bytes of codes for
+// all four steps of the stage, and their one E8M0 scale.
+template <class C, int MB, bool MX = C::MX>
 struct Frags2 {
     bf16x8 a[2][MB];
-    WFrag<C::MX> b[2][C::NMAT][C::NBW];
+    bf16x8 b[2][C::NMAT][C::NBW];
+};
+template <class C, int MB>
+struct Frags2<C, MB, true> {
+    bf16x8 a[2][MB];
+    u32x4 codes[C::NMAT][C::NBW];
+    uint32_t scale[C::NMAT][C::NBW];
 };
 
+// K order inside a 64-wide stage.  A 32x32x16 MFMA step q takes, in lane half
+// h = l / 32, eight consecutive K elements of the row; any assignment of the
+// stage's eight 8-element chunks to (q, h) gives the same contraction as long
+// as both operands use it.  bf16 weights: chunk 2q + h.  MXFP4 weights: chunk
+// 4h + q, so that a lane half's four steps span one 32-element scale group and
+// its codes for the whole stage are 16 contiguous bytes (one LDS read, one
+// scale per stage).
+template <bool MX>
+__device__ __forceinline__ int stage_chunk(int q, int h) { return MX ? 4 * h + q : 2 * q + h; }
+
 // Fragments of K step q: lane offset within a 4-block (32-row) group.
+template <bool MX>
 __device__ __forceinline__ uint32_t frag_lane_off(int lane, int q) {
     const int r = lane & 31, rb = lane & 7;
-    const int c = 2 * q + (lane >> 5);
+    const int c = stage_chunk<MX>(q, lane >> 5);
     return (uint32_t)((r >> 3) * 1024 + rb * 128 + ((c ^ rb ^ ((r >> 3) & 1)) * 16));
 }
+
+// MXFP4 codes in LDS: a 32-row weight group's 32 bytes per row (64 K) are
+// 16-byte slots, row r's half h (K chunks 4h .. 4h+3) in slot
+// 2r + (h ^ ((r >> 3) & 1)), which spreads every 16 lanes' 16-byte reads over
+// all 64 banks.  The DMA lane that fills slot s fetches row s / 2, half
+// (s & 1) ^ ((s >> 4) & 1).
+__device__ __forceinline__ uint32_t mx_code_slot(int r, int h) { return (uint32_t)(2 * r + (h ^ ((r >> 3) & 1))); }
 
 // MXFP4: 8 codes (4 bytes) and their E8M0 scale -> 8 bf16, exactly.
 __device__ __forceinline__ bf16x8 mx_frag(uint32_t q, uint32_t scale) {
@@ -188,42 +204,53 @@ __device__ __forceinline__ bf16x8 mx_frag(uint32_t q, uint32_t scale) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// Where a lane's MXFP4 operand lives: block row l%32, and within the row's
-// 32 bytes of codes for this stage the 4 bytes of K elements 16q + 8(l/32).
+// Where a lane's MXFP4 operand lives: its 16-byte code slot within a 32-row
+// group, and its row's scales (kg bytes per row, this stage's group 2kt + h).
 struct MxLane {
-    uint32_t code_off;   // r * 32 + 4 * (l / 32)  (+ 8q per step)
-    uint32_t scale_row;  // r * kg
+    uint32_t code_off;   // 16 * mx_code_slot(l % 32, l / 32)
+    uint32_t scale_row;  // (l % 32) * kg + l / 32
 };
 
-// Read the fragments of steps q0, q0+1 of stage kt (held at `st`).
+// Read the fragments of steps q0, q0+1 of stage kt (held at `st`).  MXFP4
+// codes and scales are read once per stage, with steps 0, 1; steps 2, 3 take
+// them from `same`, the fragments of steps 0, 1 of this stage.
 template <class C, int BN, int MB>
 __device__ __forceinline__ void read_frags2(const unsigned char* st, const uint32_t (&loff)[4], int q0, int wm, int wn,
-                                            Frags2<C, MB>& f, const unsigned char* scales, int kg, int kt,
-                                            MxLane mxl) {
+                                            Frags2<C, MB>& f, const Frags2<C, MB>& same, const unsigned char* scales,
+                                            int kg, int kt, MxLane mxl) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
             f.a[h][i] = *reinterpret_cast<const bf16x8*>(st + (wm + kWM * i) * 4096 + loff[q0 + h]);
+        if constexpr (!C::MX) {
+#pragma unroll
+            for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+                for (int j = 0; j < C::NBW; ++j) {
+                    const int grp = m * (BN / 32) + wn * C::NBW + j;  // 32-row weight group
+                    f.b[h][m][j] = *reinterpret_cast<const bf16x8*>(st + C::A_BYTES + grp * 4096 + loff[q0 + h]);
+                }
+        }
+    }
+    if constexpr (C::MX) {
 #pragma unroll
         for (int m = 0; m < C::NMAT; ++m)
 #pragma unroll
             for (int j = 0; j < C::NBW; ++j) {
-                const int grp = m * (BN / 32) + wn * C::NBW + j;  // 32-row weight group
-                if constexpr (C::MX) {
-                    const int q = q0 + h;
-                    const uint32_t codes = *reinterpret_cast<const uint32_t*>(st + C::A_BYTES + grp * 1024 +
-                                                                              mxl.code_off + 8 * q);
-                    const uint32_t scale = scales[(uint32_t)grp * 32u * (uint32_t)kg + mxl.scale_row + 2 * kt + q / 2];
-                    f.b[h][m][j].v = u32x2{codes, scale};
+                if (q0 == 0) {
+                    const int grp = m * (BN / 32) + wn * C::NBW + j;
+                    f.codes[m][j] = *reinterpret_cast<const u32x4*>(st + C::A_BYTES + grp * 1024 + mxl.code_off);
+                    f.scale[m][j] = scales[(uint32_t)grp * 32u * (uint32_t)kg + mxl.scale_row + 2 * kt];
                 } else {
-                    f.b[h][m][j].v = *reinterpret_cast<const bf16x8*>(st + C::A_BYTES + grp * 4096 + loff[q0 + h]);
+                    f.codes[m][j] = same.codes[m][j];
+                    f.scale[m][j] = same.scale[m][j];
                 }
             }
     }
 }
 
-template <class C, int MB>
+template <class C, int MB, int Q0>
 __device__ __forceinline__ void mma2(const Frags2<C, MB>& f, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -232,8 +259,8 @@ __device__ __forceinline__ void mma2(const Frags2<C, MB>& f, f32x16 (&acc)[C::NM
 #pragma unroll
             for (int j = 0; j < C::NBW; ++j) {
                 bf16x8 b;
-                if constexpr (C::MX) b = mx_frag(f.b[h][m][j].v.x, f.b[h][m][j].v.y);
-                else b = f.b[h][m][j].v;
+                if constexpr (C::MX) b = mx_frag(f.codes[m][j][Q0 + h], f.scale[m][j]);
+                else b = f.b[h][m][j];
 #pragma unroll
                 for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(f.a[h][i], b, acc[m][i][j]);
             }
@@ -297,11 +324,13 @@ template <class C, int BN, int MB, bool DMA, bool NEXT, int WAIT>
 __device__ __forceinline__ void stage_iter(const ItemCtx<C>& x, unsigned char* smem, int nk, int kt, int wave, int wm,
                                            int wn, const uint32_t (&loff)[4], Frags2<C, MB>& lo, Frags2<C, MB>& hi,
                                            f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
-    constexpr int NR = 2 * (MB + C::NMAT * C::NBW);  // fragment reads per two steps
+    // fragment reads per two steps (MXFP4: the weight codes once per stage, with the first half)
+    constexpr int NR = 2 * MB + (C::MX ? 0 : 2 * C::NMAT * C::NBW);
+    constexpr int NR0 = NR + (C::MX ? 2 * C::NMAT * C::NBW : 0);
     constexpr int NM = 2 * C::NMAT * C::NBW * MB;    // MFMAs per two steps
     const unsigned char* st = smem + (kt % C::NST) * C::STAGE;
-    read_frags2<C, BN, MB>(st, loff, 2, wm, wn, hi, x.scales, x.kg, kt, x.mxl);
-    mma2<C, MB>(lo, acc);
+    read_frags2<C, BN, MB>(st, loff, 2, wm, wn, hi, lo, x.scales, x.kg, kt, x.mxl);
+    mma2<C, MB, 0>(lo, acc);
     interleave<0, 0, NR, NM>();
     if constexpr (NEXT) {
         if constexpr (WAIT >= 0) wait_vmcnt<WAIT * C::DPS>();
@@ -309,12 +338,12 @@ __device__ __forceinline__ void stage_iter(const ItemCtx<C>& x, unsigned char* s
         wait_lds_reads();
         bare_barrier();
         if constexpr (DMA) dma_stage<C>(x.src, smem, kt + C::NST, wave, x.a_voff, x.b_voff, x.b_mat);
-        read_frags2<C, BN, MB>(smem + ((kt + 1) % C::NST) * C::STAGE, loff, 0, wm, wn, lo, x.scales, x.kg, kt + 1,
-                               x.mxl);
-        mma2<C, MB>(hi, acc);
-        interleave<0, DMA ? C::DPS : 0, NR, NM>();
+        read_frags2<C, BN, MB>(smem + ((kt + 1) % C::NST) * C::STAGE, loff, 0, wm, wn, lo, lo, x.scales, x.kg,
+                               kt + 1, x.mxl);
+        mma2<C, MB, 2>(hi, acc);
+        interleave<0, DMA ? C::DPS : 0, NR0, NM>();
     } else {
-        mma2<C, MB>(hi, acc);
+        mma2<C, MB, 2>(hi, acc);
     }
 }
 
@@ -325,12 +354,12 @@ __device__ __forceinline__ void main_loop(const ItemCtx<C>& x, unsigned char* sm
     const int wm = wave >> 1, wn = wave & 1;
     uint32_t loff[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) loff[q] = frag_lane_off(lane, q);
+    for (int q = 0; q < 4; ++q) loff[q] = frag_lane_off<C::MX>(lane, q);
     Frags2<C, MB> lo, hi;
     wait_stages_ahead<C::DPS>(min(nk, C::NST) - 1);
     wait_lds_reads();  // MXFP4: this wave's scale writes
     bare_barrier();
-    read_frags2<C, BN, MB>(smem, loff, 0, wm, wn, lo, x.scales, x.kg, 0, x.mxl);
+    read_frags2<C, BN, MB>(smem, loff, 0, wm, wn, lo, lo, x.scales, x.kg, 0, x.mxl);
     int kt = 0;
     // steady state: the next stage exists and a stage NST ahead is refilled
     for (; kt + C::NST < nk; ++kt)
@@ -398,8 +427,8 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
     ItemCtx<C> x;
     x.kg = K / 32;
     x.scales = smem + C::SMEM;
-    x.mxl.code_off = (uint32_t)((lane & 31) * 32 + 4 * (lane >> 5));
-    x.mxl.scale_row = (uint32_t)((lane & 31) * x.kg);
+    x.mxl.code_off = 16u * mx_code_slot(lane & 31, lane >> 5);
+    x.mxl.scale_row = (uint32_t)((lane & 31) * x.kg + (lane >> 5));
     // ---- DMA sources: byte offsets of this lane's chunk in stage 0 ----
 #pragma unroll
     for (int i = 0; i < C::A_DMA; ++i) {
@@ -418,13 +447,13 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
         x.src.w[1] = MODE == 0 ? make_rsrc((const unsigned char*)args.w1 + (size_t)e * wb, wb) : x.src.w[0];
         x.src.s[0] = make_rsrc(args.s0 + (size_t)e * sb, sb);
         x.src.s[1] = MODE == 0 ? make_rsrc(args.s1 + (size_t)e * sb, sb) : x.src.s[0];
-        // 32-row blocks of codes: lane l fetches row l/2, bytes 16(l%2)..+15 of the stage's 32
+        // 32-row blocks of codes: lane l fills slot l, i.e. row l/2, half (l%2) ^ ((l/16)%2) of the stage's 32 bytes
 #pragma unroll
         for (int i = 0; i < C::B_DMA; ++i) {
             const int blk = wave + kWaves * i;
             x.b_mat[i] = (blk * 32) / BN;
             const int n = min(n0 + (blk * 32) % BN + (lane >> 1), N - 1);
-            x.b_voff[i] = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)(lane & 1) * 16u;
+            x.b_voff[i] = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)((lane & 1) ^ ((lane >> 4) & 1)) * 16u;
         }
         // the tile's scales for all of K: [matrix][BN rows][kg], rows past N read as zero
         const int per_mat = BN * x.kg;  // bytes, a multiple of 16
