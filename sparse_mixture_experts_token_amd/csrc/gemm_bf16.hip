@@ -157,7 +157,7 @@ template <class C, int MB>
 struct Frags2<C, MB, true> {
     bf16x8 a[2][MB];
     u32x4 codes[C::NMAT][C::NBW];
-    uint32_t scale[C::NMAT][C::NBW];
+    float sc[C::NMAT][C::NBW];  // 2^(scale - 127) as the fp32 with exponent field `scale`
 };
 
 // K order inside a 64-wide stage.  A 32x32x16 MFMA step q takes, in lane half
@@ -185,14 +185,20 @@ __device__ __forceinline__ uint32_t frag_lane_off(int lane, int q) {
 // (s & 1) ^ ((s >> 4) & 1).
 __device__ __forceinline__ uint32_t mx_code_slot(int r, int h) { return (uint32_t)(2 * r + (h ^ ((r >> 3) & 1))); }
 
-// MXFP4: 8 codes (4 bytes) and their E8M0 scale -> 8 bf16, exactly.
-__device__ __forceinline__ bf16x8 mx_frag(uint32_t q, uint32_t scale) {
+// MXFP4: 8 codes (4 bytes) and their E8M0 scale -> 8 bf16, exactly.  For
+// scales 2..252 every product is a normal bf16 (or zero) and the hardware
+// scaled conversion is exact; EXACT takes the integer path that also covers
+// the extremes (subnormal results, overflow, the NaN scale).  `sc` is the
+// scale's fp32 (exponent field = scale), from which the integer path takes
+// the scale back.
+template <bool EXACT>
+__device__ __forceinline__ bf16x8 mx_frag(uint32_t q, float sc) {
     u32x4 v;
-    if (scale >= 2u && scale <= 252u) {
-        const float sc = __uint_as_float(scale << 23);
+    if constexpr (!EXACT) {
         v = u32x4{cvt_fp4x2_bf16x2(q, sc, 0), cvt_fp4x2_bf16x2(q, sc, 1), cvt_fp4x2_bf16x2(q, sc, 2),
                   cvt_fp4x2_bf16x2(q, sc, 3)};
     } else {
+        const uint32_t scale = __float_as_uint(sc) >> 23;
         uint32_t w[4];
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
@@ -241,16 +247,19 @@ __device__ __forceinline__ void read_frags2(const unsigned char* st, const uint3
                 if (q0 == 0) {
                     const int grp = m * (BN / 32) + wn * C::NBW + j;
                     f.codes[m][j] = *reinterpret_cast<const u32x4*>(st + C::A_BYTES + grp * 1024 + mxl.code_off);
-                    f.scale[m][j] = scales[(uint32_t)grp * 32u * (uint32_t)kg + mxl.scale_row + 2 * kt];
+                    const uint32_t raw = scales[(uint32_t)grp * 32u * (uint32_t)kg + mxl.scale_row + 2 * kt];
+                    f.sc[m][j] = __uint_as_float(raw << 23);
                 } else {
                     f.codes[m][j] = same.codes[m][j];
-                    f.scale[m][j] = same.scale[m][j];
+                    f.sc[m][j] = same.sc[m][j];
                 }
             }
     }
 }
 
-template <class C, int MB, int Q0>
+// Steps Q0, Q0+1.  EXACT (MXFP4 only): decode on the integer path, for tiles
+// with a scale outside 2..252.
+template <class C, int MB, int Q0, bool EXACT>
 __device__ __forceinline__ void mma2(const Frags2<C, MB>& f, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -259,12 +268,14 @@ __device__ __forceinline__ void mma2(const Frags2<C, MB>& f, f32x16 (&acc)[C::NM
 #pragma unroll
             for (int j = 0; j < C::NBW; ++j) {
                 bf16x8 b;
-                if constexpr (C::MX) b = mx_frag(f.codes[m][j][Q0 + h], f.scale[m][j]);
+                if constexpr (C::MX) b = mx_frag<EXACT>(f.codes[m][j][Q0 + h], f.sc[m][j]);
                 else b = f.b[h][m][j];
 #pragma unroll
                 for (int i = 0; i < MB; ++i) acc[m][i][j] = mfma32(f.a[h][i], b, acc[m][i][j]);
             }
 }
+
+
 
 struct Srcs {
     buf_rsrc a;
@@ -303,6 +314,23 @@ __device__ __forceinline__ void interleave() {
     }
 }
 
+// MXFP4 tiles: each wave's verdict on the part of the tile's scales it
+// copied into LDS (nonzero: a scale of a live weight row outside 2..252, so
+// the tile decodes on the integer path).  Written during the item's set-up,
+// read after the main loop's first barrier.
+__device__ __forceinline__ int* wave_verdicts() {
+    __shared__ int s_odd[kWaves];
+    return s_odd;
+}
+
+__device__ __forceinline__ bool tile_needs_exact() {
+    const int* v = wave_verdicts();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) any |= v[w];
+    return __builtin_amdgcn_readfirstlane(any) != 0;
+}
+
 // Everything a work item's main loop needs besides the accumulators.
 template <class C>
 struct ItemCtx {
@@ -320,7 +348,7 @@ struct ItemCtx {
 // refilled with stage kt+NST (DMA) and steps 0,1 of stage kt+1 are read while
 // steps 2,3 compute.  WAIT = stages allowed in flight at the wait (-1: read
 // `ahead` at run time).
-template <class C, int BN, int MB, bool DMA, bool NEXT, int WAIT>
+template <class C, int BN, int MB, bool EXACT, bool DMA, bool NEXT, int WAIT>
 __device__ __forceinline__ void stage_iter(const ItemCtx<C>& x, unsigned char* smem, int nk, int kt, int wave, int wm,
                                            int wn, const uint32_t (&loff)[4], Frags2<C, MB>& lo, Frags2<C, MB>& hi,
                                            f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
@@ -330,7 +358,7 @@ __device__ __forceinline__ void stage_iter(const ItemCtx<C>& x, unsigned char* s
     constexpr int NM = 2 * C::NMAT * C::NBW * MB;    // MFMAs per two steps
     const unsigned char* st = smem + (kt % C::NST) * C::STAGE;
     read_frags2<C, BN, MB>(st, loff, 2, wm, wn, hi, lo, x.scales, x.kg, kt, x.mxl);
-    mma2<C, MB, 0>(lo, acc);
+    mma2<C, MB, 0, EXACT>(lo, acc);
     interleave<0, 0, NR, NM>();
     if constexpr (NEXT) {
         if constexpr (WAIT >= 0) wait_vmcnt<WAIT * C::DPS>();
@@ -340,11 +368,24 @@ __device__ __forceinline__ void stage_iter(const ItemCtx<C>& x, unsigned char* s
         if constexpr (DMA) dma_stage<C>(x.src, smem, kt + C::NST, wave, x.a_voff, x.b_voff, x.b_mat);
         read_frags2<C, BN, MB>(smem + ((kt + 1) % C::NST) * C::STAGE, loff, 0, wm, wn, lo, lo, x.scales, x.kg,
                                kt + 1, x.mxl);
-        mma2<C, MB, 2>(hi, acc);
+        mma2<C, MB, 2, EXACT>(hi, acc);
         interleave<0, DMA ? C::DPS : 0, NR0, NM>();
     } else {
-        mma2<C, MB, 2>(hi, acc);
+        mma2<C, MB, 2, EXACT>(hi, acc);
     }
+}
+
+template <class C, int BN, int MB, bool EXACT>
+__device__ __forceinline__ void main_loop_body(const ItemCtx<C>& x, unsigned char* smem, int nk, int wave, int wm,
+                                               int wn, const uint32_t (&loff)[4], Frags2<C, MB>& lo,
+                                               Frags2<C, MB>& hi, f32x16 (&acc)[C::NMAT][C::MBW][C::NBW]) {
+    int kt = 0;
+    // steady state: the next stage exists and a stage NST ahead is refilled
+    for (; kt + C::NST < nk; ++kt)
+        stage_iter<C, BN, MB, EXACT, true, true, C::NST - 2>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
+    for (; kt + 1 < nk; ++kt)
+        stage_iter<C, BN, MB, EXACT, false, true, -1>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
+    stage_iter<C, BN, MB, EXACT, false, false, 0>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
 }
 
 // Stages 0 .. min(NST, nk) - 1 were issued by the caller.
@@ -360,12 +401,13 @@ __device__ __forceinline__ void main_loop(const ItemCtx<C>& x, unsigned char* sm
     wait_lds_reads();  // MXFP4: this wave's scale writes
     bare_barrier();
     read_frags2<C, BN, MB>(smem, loff, 0, wm, wn, lo, lo, x.scales, x.kg, 0, x.mxl);
-    int kt = 0;
-    // steady state: the next stage exists and a stage NST ahead is refilled
-    for (; kt + C::NST < nk; ++kt)
-        stage_iter<C, BN, MB, true, true, C::NST - 2>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
-    for (; kt + 1 < nk; ++kt) stage_iter<C, BN, MB, false, true, -1>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
-    stage_iter<C, BN, MB, false, false, 0>(x, smem, nk, kt, wave, wm, wn, loff, lo, hi, acc);
+    if constexpr (C::MX) {
+        // the waves' verdicts on the tile's scales, written before the barrier above
+        if (tile_needs_exact()) main_loop_body<C, BN, MB, true>(x, smem, nk, wave, wm, wn, loff, lo, hi, acc);
+        else main_loop_body<C, BN, MB, false>(x, smem, nk, wave, wm, wn, loff, lo, hi, acc);
+    } else {
+        main_loop_body<C, BN, MB, false>(x, smem, nk, wave, wm, wn, loff, lo, hi, acc);
+    }
 }
 
 // A wave with no live row group (the short last tile of an expert) still
@@ -455,12 +497,24 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
             const int n = min(n0 + (blk * 32) % BN + (lane >> 1), N - 1);
             x.b_voff[i] = (uint32_t)n * (uint32_t)(K / 2) + (uint32_t)((lane & 1) ^ ((lane >> 4) & 1)) * 16u;
         }
-        // the tile's scales for all of K: [matrix][BN rows][kg], rows past N read as zero
+        // the tile's scales for all of K: [matrix][BN rows][kg], rows past N
+        // read as zero; the bytes of live rows are checked on the way
         const int per_mat = BN * x.kg;  // bytes, a multiple of 16
+        const int live = min(BN, N - n0) * x.kg;
         unsigned char* sc = smem + C::SMEM;
+        uint32_t odd = 0;
         for (int m = 0; m < C::NMAT; ++m)
-            for (int c = tid * 16; c < per_mat; c += kThreads * 16)
-                *reinterpret_cast<u32x4*>(sc + m * per_mat + c) = buf_load16(x.src.s[m], (uint32_t)(n0 * x.kg + c), 0);
+            for (int c = tid * 16; c < per_mat; c += kThreads * 16) {
+                const u32x4 v = buf_load16(x.src.s[m], (uint32_t)(n0 * x.kg + c), 0);
+                *reinterpret_cast<u32x4*>(sc + m * per_mat + c) = v;
+#pragma unroll
+                for (int b = 0; b < 16; ++b) {
+                    const uint32_t raw = (v[b >> 2] >> (8 * (b & 3))) & 0xffu;
+                    odd |= (uint32_t)(c + b < live) & (uint32_t)(raw - 2u > 250u);
+                }
+            }
+        const uint64_t ballot = __builtin_amdgcn_ballot_w64(odd != 0);
+        if (lane == 0) wave_verdicts()[wave] = ballot != 0;
     } else {
         const uint32_t wbytes = (uint32_t)((size_t)N * K * 2);
         x.src.w[0] = make_rsrc((const unsigned char*)args.w0 + (size_t)e * wbytes, wbytes);

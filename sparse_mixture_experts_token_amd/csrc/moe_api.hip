@@ -2,6 +2,7 @@
 // checks, workspace layout, stage launches on the caller's stream, the
 // pre-normalised block entry point, the silent expansion and the per-stage
 // timing hooks.
+#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -59,7 +60,14 @@ ForkRes g_fork[kMaxDevices];
 // Prefill passes with at least this many (token, slot) rows fork.
 constexpr int64_t kForkMinRows = 8192;
 
+// MOE_SINGLE_STREAM=1 in the environment keeps every launch on the
+// caller's stream (one launch per GEMM), read once per process.
 ForkRes* fork_res(hipStream_t stream) {
+    static const bool single = [] {
+        const char* v = std::getenv("MOE_SINGLE_STREAM");
+        return v && v[0] == '1';
+    }();
+    if (single) return nullptr;
     int dev = -1;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
     if (stream) {

@@ -128,14 +128,15 @@ def reference_out(layer: synth.Layer, stacked: dict, T: int, idx: np.ndarray, to
     """fp64 outputs of the first ``T`` tokens of a workload with selection
     ``idx`` (cached: the full-size layers take tens of seconds)."""
     c = layer.cfg
-    key = (c, T, hash(idx.tobytes()), None if tokens is None else hash(np.asarray(tokens).tobytes()))
+    # keyed by the weights object too (each entry keeps it alive, so its id is not reused)
+    key = (c, T, id(stacked), hash(idx.tobytes()), None if tokens is None else hash(np.asarray(tokens).tobytes()))
     if key not in _ref_cache:
         if len(_ref_cache) > 4:
             _ref_cache.clear()
         ow = oracle_weights(layer, stacked)
         h64 = oracle.widen(layer.h[:T], c.act)
-        _ref_cache[key] = oracle.moe_forward(h64, ow, c.k, idx=idx, tokens=tokens, workers=workers())["out"]
-    return _ref_cache[key]
+        _ref_cache[key] = (stacked, oracle.moe_forward(h64, ow, c.k, idx=idx, tokens=tokens, workers=workers())["out"])
+    return _ref_cache[key][1]
 
 
 def check_layer(layer: synth.Layer, stacked: dict, w_dev: dict | None = None, tokens=None, T: int | None = None):

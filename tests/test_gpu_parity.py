@@ -76,6 +76,32 @@ EDGE = [
 ]
 
 
+def test_mxfp4_prefill_integer_decode_matches_hardware_decode():
+    """The prefill GEMMs decode an MXFP4 tile with the hardware scaled
+    conversion when every scale of its live weight rows is in 2..252, else
+    on the integer path.  Scale group 1 of a few weight rows gets all-zero
+    codes (it contributes exactly nothing) and scale 0 (integer path for the
+    tiles holding those rows) or 120 (hardware path): the outputs must be
+    bitwise equal, so the integer path reproduces the hardware decode on
+    every other group, and both match the fp64 reference.  Gate row 3 of
+    experts 0-4 (gate/up column tile 0 only) and down row 70 of experts 5-8
+    are changed, so both paths run in each launch."""
+    cfg = next(c for c in EDGE if c.name == "mxfp4-small")
+    L = synth.make_layer(cfg)
+    base = L.stacked()
+    outs = []
+    for scale in (0, 120):
+        st = {n: a.copy() for n, a in base.items()}
+        for e in range(cfg.E):
+            n, row = ("gate", 3) if e < 5 else ("down", 70)
+            st[n][e, row, 16:32] = 0      # packed codes of K elements 32..63
+            st["s_" + n][e, row, 1] = scale
+        m, g = check_layer(L, st)
+        print(scale, m)
+        outs.append(g["out_raw"])
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
 @pytest.mark.parametrize("cfg", EDGE, ids=[c.name for c in EDGE])
 def test_edge_shapes(cfg):
     L = synth.make_layer(cfg)
