@@ -26,10 +26,15 @@
 // row in one 16-byte load plus exactly one E8M0 scale, and feeds them to the
 // four steps as elements 8j..8j+7; a contraction is unchanged by a
 // permutation of K applied to both operands, so the activation operand is
-// read in the same permuted order.  All loads of a K step are issued before
-// its MFMAs (scheduling barriers keep the compiler from interleaving them,
-// which would leave only a few loads in flight); the down product also keeps
-// the next step's loads in flight while multiplying.
+// read in the same permuted order.  Two consecutive MXFP4 steps read the two
+// halves of the same 128-byte line of each weight row: their loads go out as
+// adjacent instructions, in pairs of steps, which lets the L1 merge them
+// (issued a step apart they went to L2 as separate requests).  All loads of
+// a K step are issued before its MFMAs (scheduling barriers keep the
+// compiler from interleaving them, which would leave only a few loads in
+// flight); the bf16 down product keeps the next step's loads in flight while
+// multiplying, the MXFP4 kernels the second step of a pair while they
+// multiply the first.
 //
 // Work split.  bf16 gate/up runs with one workgroup per CU: the (tile, weight
 // row) pairs are split into equal contiguous ranges, one per workgroup, and
@@ -132,16 +137,58 @@ __device__ __forceinline__ void issue(Batch<MODE, WDT, NP>& x, buf_rsrc w0, buf_
     load_b<WDT>(bsrc, b_base, has_row, K, g, qd, x.b);
 }
 
-template <int WDT, int NQ>
+// MXFP4, staged scales: steps g and g+1 (g even) read the two halves of the
+// same 128-byte line of every weight row; their loads go out adjacent.
+template <int MODE, int NP>
+__device__ __forceinline__ void issue_pair(Batch<MODE, DT_MXFP4, NP>& x, Batch<MODE, DT_MXFP4, NP>& y, buf_rsrc w0,
+                                           buf_rsrc w1, buf_rsrc bsrc, const uint32_t (&n)[NP],
+                                           const bool (&nv)[NP], uint32_t b_base, bool has_row, uint32_t K,
+                                           uint32_t g, uint32_t qd) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const uint32_t kq0 = g * 128 + qd * 32, kq1 = kq0 + 128;
+        const uint32_t c0 = (nv[p] && kq0 < K) ? n[p] * (K / 2) + kq0 / 2 : kOob;
+        const uint32_t c1 = (nv[p] && kq1 < K) ? n[p] * (K / 2) + kq1 / 2 : kOob;
+        x.wq[p] = buf_load16(w0, c0, 0);
+        y.wq[p] = buf_load16(w0, c1, 0);
+        if constexpr (MODE == 0) {
+            x.uq[p] = buf_load16(w1, c0, 0);
+            y.uq[p] = buf_load16(w1, c1, 0);
+        }
+    }
+    load_b<DT_MXFP4>(bsrc, b_base, has_row, K, g, qd, x.b);
+    load_b<DT_MXFP4>(bsrc, b_base, has_row, K, g + 1, qd, y.b);
+}
+
+template <int PATH, int NQ>
 __device__ __forceinline__ void frags(const u32x4 (&q)[NQ], uint32_t scale, int p, bf16x8 (&f)[4]) {
     uint32_t d[16];
-    decode_mxfp4_32(q[p], scale, d);
+    decode_mxfp4_32<PATH>(q[p], scale, d);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
         f[j] = __builtin_bit_cast(bf16x8, u32x4{d[4 * j], d[4 * j + 1], d[4 * j + 2], d[4 * j + 3]});
 }
 
-template <int MODE, int WDT, int NP>
+template <int MODE, int WDT, int NP, int PATH>
+__device__ __forceinline__ void compute_mx(const Batch<MODE, WDT, NP>& x, f32x4 (&acc0)[NP], f32x4 (&acc1)[NP]) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        bf16x8 fa[4];
+        frags<PATH>(x.wq, x.ws[p], p, fa);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc0[p] = mfma16(fa[j], __builtin_bit_cast(bf16x8, x.b[j]), acc0[p]);
+        if constexpr (MODE == 0) {
+            bf16x8 fu[4];
+            frags<PATH>(x.uq, x.us[p], p, fu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc1[p] = mfma16(fu[j], __builtin_bit_cast(bf16x8, x.b[j]), acc1[p]);
+        }
+    }
+}
+
+// UNIFORM (MXFP4): one decode path per wave and K step (else per lane, which
+// costs fewer registers).
+template <int MODE, int WDT, int NP, bool UNIFORM = false>
 __device__ __forceinline__ void compute(const Batch<MODE, WDT, NP>& x, f32x4 (&acc0)[NP], f32x4 (&acc1)[NP]) {
     if constexpr (WDT != DT_MXFP4) {
         // each 16-byte register straight into its MFMA (no fragment copies,
@@ -154,20 +201,19 @@ __device__ __forceinline__ void compute(const Batch<MODE, WDT, NP>& x, f32x4 (&a
                 acc0[p] = mfma16(__builtin_bit_cast(bf16x8, x.wq[4 * p + j]), bj, acc0[p]);
                 if constexpr (MODE == 0) acc1[p] = mfma16(__builtin_bit_cast(bf16x8, x.uq[4 * p + j]), bj, acc1[p]);
             }
+    } else if constexpr (!UNIFORM) {
+        compute_mx<MODE, WDT, NP, 0>(x, acc0, acc1);
     } else {
+        // one decision per wave and K step: the hardware decode unless a lane
+        // holds a scale outside 2..252
+        uint32_t odd = 0;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            bf16x8 fa[4];
-            frags<WDT>(x.wq, x.ws[p], p, fa);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc0[p] = mfma16(fa[j], __builtin_bit_cast(bf16x8, x.b[j]), acc0[p]);
-            if constexpr (MODE == 0) {
-                bf16x8 fu[4];
-                frags<WDT>(x.uq, x.us[p], p, fu);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc1[p] = mfma16(fu[j], __builtin_bit_cast(bf16x8, x.b[j]), acc1[p]);
-            }
+            odd |= (uint32_t)(x.ws[p] - 2u > 250u);
+            if constexpr (MODE == 0) odd |= (uint32_t)(x.us[p] - 2u > 250u);
         }
+        if (__builtin_amdgcn_ballot_w64(odd != 0) != 0) compute_mx<MODE, WDT, NP, 2>(x, acc0, acc1);
+        else compute_mx<MODE, WDT, NP, 1>(x, acc0, acc1);
     }
 }
 
@@ -199,8 +245,9 @@ __device__ __forceinline__ void scales_dma(buf_rsrc s0, buf_rsrc s1, uint32_t c0
         }
 }
 
-// Scales of K step g for this lane from the LDS copy (0 past K or past the
-// block, where the codes read as zeros: a NaN scale must not meet them).
+// Scales of K step g for this lane from the LDS copy (127, i.e. one, past K
+// or past the block, where the codes read as zeros: a NaN scale must not
+// meet them, and a scale in 2..252 keeps the step on the hardware decode).
 template <int MODE, int WDT, int NP>
 __device__ __forceinline__ void scales_fetch(Batch<MODE, WDT, NP>& x, const uint8_t* sl, const bool (&nv)[NP],
                                              uint32_t KG, uint32_t g, int r, uint32_t qd) {
@@ -210,8 +257,8 @@ __device__ __forceinline__ void scales_fetch(Batch<MODE, WDT, NP>& x, const uint
     for (int p = 0; p < NP; ++p) {
         const bool kv = nv[p] && grp < KG;
         const uint32_t o = (uint32_t)(p * NMAT) * seg + (uint32_t)r * KG + grp;
-        x.ws[p] = kv ? sl[o] : 0u;
-        if constexpr (MODE == 0) x.us[p] = kv ? sl[o + seg] : 0u;
+        x.ws[p] = kv ? sl[o] : 127u;
+        if constexpr (MODE == 0) x.us[p] = kv ? sl[o + seg] : 127u;
     }
 }
 
@@ -274,21 +321,21 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
         scales_dma<NP, NMAT>(s0, s1, c0, KG, sl, lane);
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
-        issue<MODE, WDT, NP, true>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, 0, qd);
+        issue_pair<MODE, NP>(x0, x1, w0, w1, bsrc, n, nv, b_base, has_row, K, 0, qd);
         // The compiler does not track the LDS writes of the copies above.  Loads
-        // retire in issue order and the first step issued NP NMAT + 4 after them,
-        // so once at most NP NMAT remain outstanding the scales are in LDS.
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NP * NMAT) : "memory");
+        // retire in issue order; the scales went out first.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NP * NMAT + 8) : "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        // a pair of steps per iteration; the next pair's loads go out behind
+        // this pair's MFMAs
         for (uint32_t g = 0; g < ng; g += 2) {
-            issue<MODE, WDT, NP, true>(x1, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 1, qd);
-            __builtin_amdgcn_sched_barrier(0);
             scales_fetch<MODE, WDT, NP>(x0, sl, nv, KG, g, r, qd);
-            compute<MODE, WDT, NP>(x0, acc0, acc1);
-            __builtin_amdgcn_sched_barrier(0);
-            issue<MODE, WDT, NP, true>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g + 2, qd);
+            compute<MODE, WDT, NP, true>(x0, acc0, acc1);
             __builtin_amdgcn_sched_barrier(0);
             scales_fetch<MODE, WDT, NP>(x1, sl, nv, KG, g + 1, r, qd);
-            compute<MODE, WDT, NP>(x1, acc0, acc1);
+            compute<MODE, WDT, NP, true>(x1, acc0, acc1);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_pair<MODE, NP>(x0, x1, w0, w1, bsrc, n, nv, b_base, has_row, K, g + 2, qd);
             __builtin_amdgcn_sched_barrier(0);
         }
     } else if constexpr (DEPTH == 1) {
@@ -376,7 +423,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_balanced_kernel(DArgs a)
 // One block of 16 NP weight rows per wave: wave q takes block q % nb of tile
 // q / nb, nb = ceil(N / (16 NP)).  SL: MXFP4 scales staged in LDS (K/32 <= kScaleMaxKg).
 template <int MODE, int WDT, int DEPTH, int NP, bool SL>
-__global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
+__device__ __forceinline__ void decode_block_body(const DArgs& a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int ntl = min(a.n_tiles[0], a.max_tiles);
     constexpr uint32_t kRows = 16 * NP;
@@ -389,6 +436,19 @@ __global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
     static_assert(!SL || kBlkWaves == 1, "staged scales are per wave");
     decode_pass<MODE, WDT, DEPTH, NP, SL>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane,
                                           dsm);
+}
+
+template <int MODE, int WDT, int DEPTH, int NP, bool SL>
+__global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
+    decode_block_body<MODE, WDT, DEPTH, NP, SL>(a);
+}
+
+// MXFP4: registers capped for three waves per SIMD (the loads in flight are
+// what the kernel's speed rests on).
+template <int MODE, int DEPTH, int NP>
+__global__ __launch_bounds__(kBlkWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_block_mx_kernel(
+    DArgs a) {
+    decode_block_body<MODE, DT_MXFP4, DEPTH, NP, true>(a);
 }
 
 // ------------------------------------------------ fused routing + gate/up --
@@ -731,7 +791,8 @@ hipError_t launch_blocks(const GemmProblem& p, hipStream_t stream) {
     static_assert(!kSL || DEPTH == 2, "staged scales: two K steps in flight");
     if (kSL && (uint32_t)a.K / 32 > kScaleMaxKg) return hipErrorInvalidValue;  // beyond the MXFP4 K limit
     const size_t smem = kSL ? (size_t)NP * (MODE == 0 ? 2 : 1) * scale_lines(a.K / 32) * 256 : 0;
-    decode_block_kernel<MODE, WDT, DEPTH, NP, kSL><<<blocks, kBlkWaves * 64, smem, stream>>>(a);
+    if constexpr (kSL) decode_block_mx_kernel<MODE, DEPTH, NP><<<blocks, kBlkWaves * 64, smem, stream>>>(a);
+    else decode_block_kernel<MODE, WDT, DEPTH, NP, false><<<blocks, kBlkWaves * 64, smem, stream>>>(a);
     return hipGetLastError();
 }
 

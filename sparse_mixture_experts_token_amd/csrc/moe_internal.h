@@ -101,9 +101,15 @@ __device__ __forceinline__ uint32_t cvt_fp4x2_bf16x2(uint32_t w, float sc, int b
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// 32 codes (16 bytes) and their E8M0 scale -> 32 bf16 (16 words), exactly.
+// PATH 1: the hardware scaled conversion, for scales 2..252 only (every
+// product is then a normal bf16 or zero); PATH 2: the integer path, any
+// scale; PATH 0: chosen per lane.  Callers that know a whole wave's scales
+// take PATH 1 or 2 and branch once for the wave.
+template <int PATH = 0>
 __device__ __forceinline__ void decode_mxfp4_32(const u32x4& q, uint32_t scale, uint32_t out[16]) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    if (scale >= 2u && scale <= 252u) {
+    if (PATH == 1 || (PATH == 0 && scale >= 2u && scale <= 252u)) {
         const float sc = __uint_as_float(scale << 23);  // 2^(scale-127), a normal float
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
