@@ -134,13 +134,7 @@ size_t moe_workspace_bytes(const moe_problem *p);
  * `routing` may be NULL.  `workspace` must hold moe_workspace_bytes(p) bytes
  * (16-byte aligned) and must not be used by anything else until the stream
  * has passed this call.
- * Streams: with bf16 activations and T*k >= 8192 the expert GEMMs run as two
- * expert parts, one on `stream` and one on a stream of the library's (one
- * per device, created on first use), forked after the routing and joined
- * before the combine: work enqueued on `stream` after this call still runs
- * after all of it, and the outputs are bitwise those of one stream.
- * MOE_SINGLE_STREAM=1 in the environment (read once per process) keeps
- * everything on `stream`.
+ * Every kernel runs on `stream`.
  * Errors: MOE_ERR_NULL (p, w, w_router, w_gate, w_up, w_down, h, out or
  * workspace NULL while T > 0; MXFP4 scales NULL), MOE_ERR_SHAPE, MOE_ERR_DTYPE,
  * MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_HIP. */
@@ -162,7 +156,6 @@ int moe_forward(const moe_problem *p, const moe_weights *w, const void *h, void 
  * and the array keeps the previous call's contents (the kernels clear what
  * must start at zero themselves), so calls that overlap on one GPU (two
  * streams, or two threads) race and must be serialised by the caller.
- * Everything runs on `stream` (no second stream).
  * `stream` must belong to the current device (else MOE_ERR_HIP). */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 int moe_forward_noalloc(const moe_problem *p, const moe_weights *w, const void *h, void *out,
@@ -184,9 +177,8 @@ int moe_forward_noalloc(const moe_problem *p, const moe_weights *w, const void *
  * rounded once to bf16.  The residual is added in fp32 to the sum of the
  * expert outputs before the single rounding of out.
  * Deterministic.  `workspace` must hold moe_block_workspace_bytes(p) bytes;
- * out must not overlap x.  `routing` and streams as in moe_forward (logits
- * are those of the normalised input).  Profiling stage 0 includes the
- * normalisation.
+ * out must not overlap x.  `routing` as in moe_forward (logits are those of
+ * the normalised input).  Profiling stage 0 includes the normalisation.
  * Errors: as moe_forward (x in the place of h), plus MOE_ERR_NULL for
  * norm_weight, MOE_ERR_ALIGN for norm_weight not 16-byte aligned and
  * MOE_ERR_SHAPE for eps negative, NaN or infinite. */

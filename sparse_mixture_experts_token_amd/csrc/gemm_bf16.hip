@@ -79,7 +79,7 @@ struct BArgs {
     const Tile* tiles;
     const int32_t* work;    // row tile * n_ntiles + column tile, expert-grouped order
     const int32_t* n_work;
-    const int32_t* bounds;  // [kXcdRanges + 1]: this launch's item range and its XCD cuts
+    const int32_t* bounds;  // [kXcdRanges + 1]
     int32_t* queue;         // [8] per-XCD work counters, zero at launch
     void* out;
     uint32_t a_bytes;
@@ -604,10 +604,8 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
     }
 }
 
-// Persistent workgroups, one per CU.  A launch takes one item range of the
-// work list (all of it, or one of the two expert parts that the layer runs
-// as concurrent launches).  Blocks are dealt round-robin to the 8
-// XCDs; XCD x owns the x-th of 8 contiguous pieces of that range, cut by
+// Persistent workgroups, one per CU.  Blocks are dealt round-robin to the 8
+// XCDs; XCD x owns the x-th of 8 contiguous ranges of the work list, cut by
 // the route scan so that their estimated costs are equal (a short row tile
 // costs less than a full one), and its workgroups take the range's items
 // in order from the XCD's counter, so a workgroup that drew cheap items (the
@@ -618,11 +616,8 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
     __shared__ int s_q;
     const int n_work = args.n_work[0];
     const int xcd = blockIdx.x % kXcds;
-    // this launch's item range, then this XCD's part of it
-    const int lo = min(max(args.bounds[0], 0), n_work);
-    const int hi = min(max(args.bounds[kXcds], lo), n_work);
-    const int base = min(max(args.bounds[xcd], lo), hi);
-    const int end = min(max(args.bounds[xcd + 1], base), hi);
+    const int base = min(max(args.bounds[xcd], 0), n_work);
+    const int end = min(max(args.bounds[xcd + 1], base), n_work);
     for (;;) {
         if (threadIdx.x == 0) s_q = base + atomicAdd(args.queue + xcd, 1);
         // s_q visible to every wave, and every wave done with the previous item's LDS
@@ -668,8 +663,8 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.N = p.I;
         a.work = p.work_gateup;
         a.n_work = p.n_work_gateup;
-        a.bounds = p.bounds_gateup + p.range * (kXcds + 1);
-        a.queue = p.queues + (2 * p.range) * kXcds;
+        a.bounds = p.bounds_gateup;
+        a.queue = p.queues;
         a.n_ntiles = (p.I + kBNGateUp - 1) / kBNGateUp;
     } else {
         a.a_src = (const uint16_t*)p.act;
@@ -683,8 +678,8 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.N = p.H;
         a.work = p.work_down;
         a.n_work = p.n_work_down;
-        a.bounds = p.bounds_down + p.range * (kXcds + 1);
-        a.queue = p.queues + (2 * p.range + 1) * kXcds;
+        a.bounds = p.bounds_down;
+        a.queue = p.queues + kXcds;
         a.n_ntiles = (p.H + kBNDown - 1) / kBNDown;
     }
     a.max_work = p.max_tiles * a.n_ntiles;

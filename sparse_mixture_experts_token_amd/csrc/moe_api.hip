@@ -2,7 +2,6 @@
 // checks, workspace layout, stage launches on the caller's stream, the
 // pre-normalised block entry point, the silent expansion and the per-stage
 // timing hooks.
-#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -40,51 +39,6 @@ int scratch_of_current_device(hipStream_t stream, char** out) {
     }
     *out = g_scratch_ptr[dev];
     return MOE_OK;
-}
-
-// A second stream and two events per device: a large prefill pass runs the
-// expert GEMMs of its two expert parts on the caller's stream and on this
-// one, forked after the route scan and joined before the combine, so that
-// one part's launches take the CUs that the other's leave idle at their
-// ends.  Created on first use; `mu` keeps one call's fork, launches and join
-// together when several host threads share a device.
-struct ForkRes {
-    hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
-    bool tried = false, ok = false;
-    std::mutex mu;
-};
-std::mutex g_fork_mu;
-ForkRes g_fork[kMaxDevices];
-
-// Prefill passes with at least this many (token, slot) rows fork.
-constexpr int64_t kForkMinRows = 8192;
-
-// MOE_SINGLE_STREAM=1 in the environment keeps every launch on the
-// caller's stream (one launch per GEMM), read once per process.
-ForkRes* fork_res(hipStream_t stream) {
-    static const bool single = [] {
-        const char* v = std::getenv("MOE_SINGLE_STREAM");
-        return v && v[0] == '1';
-    }();
-    if (single) return nullptr;
-    int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-    if (stream) {
-        hipDevice_t sdev = -1;
-        if (hipStreamGetDevice(stream, &sdev) != hipSuccess || sdev != dev) return nullptr;
-    }
-    std::lock_guard<std::mutex> g(g_fork_mu);
-    ForkRes& f = g_fork[dev];
-    if (!f.tried) {
-        f.tried = true;
-        // default priority, non-blocking: ordered only by the events below
-        f.ok = hipStreamCreateWithFlags(&f.side, hipStreamNonBlocking) == hipSuccess &&
-               hipEventCreateWithFlags(&f.fork, hipEventDisableTiming) == hipSuccess &&
-               hipEventCreateWithFlags(&f.join, hipEventDisableTiming) == hipSuccess;
-        if (!f.ok) (void)hipGetLastError();  // run unforked; leave no error for the launches
-    }
-    return f.ok ? &f : nullptr;
 }
 
 constexpr size_t kAlign = 256;
@@ -144,8 +98,8 @@ Layout layout(const moe_problem* p, int router_dt = -1, bool all_plogits = false
     L.perm = o;     o = align_up(o + tk * 4);
     L.inv = o;      o = align_up(o + tk * 4);
     L.tiles = o;    o = align_up(o + (size_t)L.max_tiles * sizeof(Tile));
-    L.ntiles = o;   o = align_up(o + 512);  // tile count, the two work-list counts, then at ints 16 and 48
-                                            // the two lists' cut points
+    L.ntiles = o;   o = align_up(o + 256);  // tile count, the two work-list counts, then at ints 16 and 32
+                                            // the two lists' XCD range bounds
     L.queues = o;   o = align_up(o + moe::kNumQueues * 4);
     // column tiles of the prefill work lists (the decode kernels need none)
     // (only the bf16-activation prefill kernels walk work lists)
@@ -287,11 +241,8 @@ struct PassIn {
     uint16_t* wlo;
 };
 
-// may_fork: the expert GEMMs of a large prefill pass may run as two
-// concurrent parts (on a second stream of the library's); false keeps every
-// launch on `stream`.
 int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void* out, const moe_routing* routing,
-             char* ws, const Layout& L, hipStream_t stream, bool may_fork) {
+             char* ws, const Layout& L, hipStream_t stream) {
     int32_t* topk_idx = (routing && routing->topk_idx) ? routing->topk_idx : (int32_t*)(ws + L.topk_idx);
     float* topk_w = (routing && routing->topk_w) ? routing->topk_w : (float*)(ws + L.topk_w);
     int32_t* offsets = (routing && routing->expert_offsets) ? routing->expert_offsets : (int32_t*)(ws + L.offsets);
@@ -312,9 +263,8 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     };
 
     hipError_t e = hipSuccess;
-    static_assert(16 + moe::kBoundsPerList <= 48 && 48 + moe::kBoundsPerList <= 128, "cut points fit the region");
     moe::WorkList wl0{L.lists ? (int32_t*)(ws + L.work0) : nullptr, ntiles + 1, L.nc0, ntiles + 16};
-    moe::WorkList wl1{L.lists ? (int32_t*)(ws + L.work1) : nullptr, ntiles + 2, L.nc1, ntiles + 48};
+    moe::WorkList wl1{L.lists ? (int32_t*)(ws + L.work1) : nullptr, ntiles + 2, L.nc1, ntiles + 32};
     int32_t* queues = (int32_t*)(ws + L.queues);
     float* part = (float*)(ws + L.part);
     mark(0);
@@ -363,36 +313,17 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     g.y = y;
     g.decode = L.decode;
     g.queues = queues;
-    // Two expert parts on two streams: not while recording stage boundaries
-    // (the stage times would mix), and only for large prefill passes.
-    ForkRes* fk = (may_fork && L.lists && !ev && (int64_t)p->T * p->k >= kForkMinRows) ? fork_res(stream) : nullptr;
-    if (fk) {
-        std::lock_guard<std::mutex> lk(fk->mu);
-        if (hipEventRecord(fk->fork, stream) != hipSuccess || hipStreamWaitEvent(fk->side, fk->fork, 0) != hipSuccess)
-            return MOE_ERR_HIP;
-        for (int r = 1; r <= 2; ++r) {
-            hipStream_t s = r == 1 ? stream : fk->side;
-            g.range = r;
-            e = moe::launch_gateup(g, s);
-            if (e == hipSuccess) e = moe::launch_down(g, s);
-            if (e != hipSuccess) return MOE_ERR_HIP;
-        }
-        if (hipEventRecord(fk->join, fk->side) != hipSuccess || hipStreamWaitEvent(stream, fk->join, 0) != hipSuccess)
-            return MOE_ERR_HIP;
+    if (L.fused) {
+        const moe::FusedRouting fr{part, in.b_router, logits, topk_idx, topk_w, offsets, perm, inv, tiles, ntiles};
+        e = moe::launch_route_gateup_decode(g, fr, stream);
     } else {
-        g.range = 0;
-        if (L.fused) {
-            const moe::FusedRouting fr{part, in.b_router, logits, topk_idx, topk_w, offsets, perm, inv, tiles, ntiles};
-            e = moe::launch_route_gateup_decode(g, fr, stream);
-        } else {
-            e = moe::launch_gateup(g, stream);
-        }
-        if (e != hipSuccess) return MOE_ERR_HIP;
-        mark(3);
-        e = moe::launch_down(g, stream);
-        if (e != hipSuccess) return MOE_ERR_HIP;
-        mark(4);
+        e = moe::launch_gateup(g, stream);
     }
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(3);
+    e = moe::launch_down(g, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(4);
     e = moe::launch_combine(p->act_dtype, y, out, p->T, p->H, p->k, in.residual, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
     mark(5);
@@ -443,7 +374,7 @@ int moe_forward(const moe_problem* p, const moe_weights* w, const void* h, void*
     in.b_router = w->b_router;
     in.gemm_h = h;
     return run_pass(p, w, in, out, routing, reinterpret_cast<char*>(workspace), L,
-                    reinterpret_cast<hipStream_t>(stream_v), true);
+                    reinterpret_cast<hipStream_t>(stream_v));
 }
 
 int moe_forward_noalloc(const moe_problem* p, const moe_weights* w, const void* h, void* out,
@@ -464,8 +395,7 @@ int moe_forward_noalloc(const moe_problem* p, const moe_weights* w, const void* 
     in.w_router = w->w_router;
     in.b_router = w->b_router;
     in.gemm_h = h;
-    // one stream: the second stream's set-up is left to the allocating entry points
-    return run_pass(p, w, in, out, routing, ws, L, stream, false);
+    return run_pass(p, w, in, out, routing, ws, L, stream);
 }
 
 size_t moe_block_workspace_bytes(const moe_problem* p) {
@@ -512,7 +442,7 @@ int moe_block_forward(const moe_problem* p, const moe_weights* w, const void* no
         in.w_router = w->w_router;
         in.gemm_h = in.n32;
     }
-    return run_pass(p, w, in, out, routing, ws, B.L, reinterpret_cast<hipStream_t>(stream_v), true);
+    return run_pass(p, w, in, out, routing, ws, B.L, reinterpret_cast<hipStream_t>(stream_v));
 }
 
 size_t moe_backward_workspace_bytes(const moe_problem* p) {

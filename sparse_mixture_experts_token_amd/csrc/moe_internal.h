@@ -231,18 +231,13 @@ hipError_t launch_router(int act_dtype, const void* h, const void* w_router, con
 // A work list enumerates (row tile, column tile) pairs as
 // tile * n_col_tiles + col_tile, grouped by expert: for each expert, for each
 // column tile, that expert's row tiles.
-// Its cut points: for each of kListRanges item ranges (0: the whole list,
-// 1: the experts before the split expert, 2: the rest), kXcdRanges + 1
-// bounds of XCD ranges of equal estimated cost.
-constexpr int kXcdRanges = 8;
-constexpr int kListRanges = 3;
-constexpr int kBoundsPerList = kListRanges * (kXcdRanges + 1);
 struct WorkList {
     int32_t* items;    // [max_tiles * n_col_tiles]
     int32_t* count;    // [1]
     int n_col_tiles;
-    int32_t* bounds;   // [kListRanges][kXcdRanges + 1]
+    int32_t* bounds;   // [kXcdRanges + 1]: item ranges of equal estimated cost, one per XCD
 };
+constexpr int kXcdRanges = 8;
 // Estimated cost of a (row tile, column tile) item: a fixed part (the weight
 // panel's DMA, which a short tile pays in full) plus one per live 32-row
 // group; per work list (gate/up, down).
@@ -275,16 +270,14 @@ struct GemmProblem {
     const int32_t* n_work_gateup;
     const int32_t* work_down;
     const int32_t* n_work_down;
-    const int32_t* bounds_gateup;  // [kListRanges][kXcdRanges + 1] XCD item ranges
+    const int32_t* bounds_gateup;  // [kXcdRanges + 1] item range of each XCD
     const int32_t* bounds_down;
-    int range;  // which item range of the work lists a prefill launch takes (0: all)
     void* act;  // [T*k, I] act_dtype (expert-major rows)
     float* y;   // [T*k, H] fp32, indexed by assignment t*k+slot
     bool decode;  // use the skinny (decode) kernels; tiles are decode_block_m() rows
-    int32_t* queues;  // [kNumQueues] work-queue counters, zeroed by the route scan: 8 per
-                      // (item range, list), at (2 * range + list) * 8
+    int32_t* queues;  // [16] work-queue counters (gate/up 0..7, down 8..15), zeroed by the route scan
 };
-constexpr int kNumQueues = 2 * kListRanges * kXcdRanges;
+constexpr int kNumQueues = 16;
 int gemm_block_m(int act_dtype, int expert_dtype, int T, int k, int E);
 // bf16-weight prefill kernels (gemm_bf16.hip)
 int bf16_block_m();

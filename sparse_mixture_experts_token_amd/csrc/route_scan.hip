@@ -11,8 +11,7 @@
 //               grouped GEMMs walk; experts without tokens get no tile.
 //   work lists  the order in which the GEMM workgroups take (row tile, column
 //               tile) pairs: expert by expert, for each column tile all of the
-//               expert's row tiles; with the cut points of the whole list and
-//               of its two parts (experts before and from a split expert).
+//               expert's row tiles.
 //
 // One workgroup of 1024 threads.  Input: the per-token-tile expert counts and
 // the within-tile ranks written by the router stage.
@@ -50,15 +49,12 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     __shared__ int32_t wsum[16];
     __shared__ int32_t wtile[16];
     __shared__ int32_t csum[2][16];
-    __shared__ int32_t s_split;     // first expert of the second part
-    __shared__ int32_t s_scost[2];  // each list's cost before the second part
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int nblk = (T + kRouterTokens - 1) / kRouterTokens;
     if (tid < n_zero) zero[tid] = 0;
-    if (tid == 0) s_split = 0;
 
     // 1. per expert: exclusive scan of its tile counts (in place) and its total.
     //    A lane owns kPer consecutive blocks, so a row of up to 64 * kPer
@@ -150,21 +146,16 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
         if (w1.count) w1.count[0] = toff[E] * w1.n_col_tiles;
     }
 
-    // 3b. cut points.  The experts are split at an expert boundary into two
-    //     parts of about equal gate/up cost: a part's down items read only
-    //     rows that its own gate/up items write, so the parts can run as
-    //     concurrent launches.  Each work list gets kListRanges item ranges
-    //     (the whole list, the first part, the second part), each cut into
-    //     kXcdRanges contiguous XCD ranges of equal estimated cost.  Expert
-    //     e's items cost nc * se (se: one column of its tiles); the experts'
-    //     cost intervals, from a block scan, partition [0, total), and the
-    //     expert whose interval holds a target finds the first of its items
-    //     that starts at or past it, then moves the cut to the nearer end of
-    //     that column tile's row tiles.
+    // 3b. each work list cut into kXcdRanges contiguous ranges of equal
+    //     estimated cost.  Expert e's items cost nc * se (se: one column of its
+    //     tiles); the experts' cost intervals, from a block scan, partition
+    //     [0, total), and the expert whose interval holds x * total / 8 finds
+    //     the first of its items that starts at or past that cost, then
+    //     moves the cut to the nearer end of that column tile's row tiles.
     {
         int groups = 0;  // live 32-row groups over this expert's tiles
         for (int j = 0; j < nt; ++j) groups += (min(BM, cnt - j * BM) + 31) / 32;
-        int se[2], ce[2], xc[2], pe[2], tot[2];
+        int se[2], ce[2], xc[2];
 #pragma unroll
         for (int l = 0; l < 2; ++l) {
             se[l] = kItemFixedCost[l] * nt + groups;
@@ -175,52 +166,26 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
         __syncthreads();
 #pragma unroll
         for (int l = 0; l < 2; ++l) {
-            int bc = 0;
-            tot[l] = 0;
-            for (int ww = 0; ww < 16; ++ww) {
-                if (ww < wave) bc += csum[l][ww];
-                tot[l] += csum[l][ww];
-            }
-            pe[l] = bc + xc[l] - ce[l];  // cost of the experts before this one
-        }
-        // the split: the expert boundary nearest half of the gate/up cost
-        // (s_split stays 0 when there is no work)
-        if (ce[0] > 0) {
-            const int half = tot[0] / 2;
-            if (pe[0] <= half && half < pe[0] + ce[0]) s_split = (half - pe[0] < pe[0] + ce[0] - half) ? tid : tid + 1;
-        }
-        __syncthreads();
-        const int es = s_split;
-        if (tid == es && es < E) {
-            s_scost[0] = pe[0];
-            s_scost[1] = pe[1];
-        }
-        if (tid == 0 && es >= E) {
-            s_scost[0] = tot[0];
-            s_scost[1] = tot[1];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int l = 0; l < 2; ++l) {
             const WorkList& w = l ? w1 : w0;
             if (!w.items || !w.bounds) continue;  // uniform
             const int nc = w.n_col_tiles;
-            const int split_cost = s_scost[l];
-            for (int r = 0; r < kListRanges; ++r) {
-                const int lo = r == 2 ? split_cost : 0, hi = r == 1 ? split_cost : tot[l];
-                const int ilo = r == 2 ? toff[es] * nc : 0, ihi = r == 1 ? toff[es] * nc : toff[E] * nc;
-                int32_t* bd = w.bounds + r * (kXcdRanges + 1);
-                if (tid == 0) {
-                    bd[0] = ilo;
-                    bd[kXcdRanges] = ihi;
-                    if (hi <= lo)
-                        for (int x = 1; x < kXcdRanges; ++x) bd[x] = ilo;
-                }
-                if (hi <= lo || ce[l] == 0) continue;
+            int bc = 0, tot = 0;
+            for (int ww = 0; ww < 16; ++ww) {
+                if (ww < wave) bc += csum[l][ww];
+                tot += csum[l][ww];
+            }
+            const int pe = bc + xc[l] - ce[l];
+            if (tid == 0) {
+                w.bounds[0] = 0;
+                w.bounds[kXcdRanges] = toff[E] * nc;
+                if (tot == 0)
+                    for (int x = 1; x < kXcdRanges; ++x) w.bounds[x] = 0;
+            }
+            if (ce[l] > 0) {
                 for (int x = 1; x < kXcdRanges; ++x) {
-                    const int target = lo + (int)((long long)(hi - lo) * x / kXcdRanges);
-                    if (target < pe[l] || target >= pe[l] + ce[l]) continue;
-                    const int rem0 = target - pe[l];
+                    const long long target = (long long)tot * x / kXcdRanges;
+                    if (target < pe || target >= (long long)pe + ce[l]) continue;
+                    const int rem0 = (int)(target - pe);
                     const int c = rem0 / se[l];
                     const int rem = rem0 - c * se[l];
                     int j = 0, acc = 0;
@@ -231,7 +196,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
                     // snap to the nearer end of column tile c's row tiles, so
                     // that one XCD runs all of them and its L2 serves the
                     // weight panel's repeats
-                    bd[x] = toff[tid] * nc + (2 * j <= nt ? c : c + 1) * nt;
+                    w.bounds[x] = toff[tid] * nc + (2 * j <= nt ? c : c + 1) * nt;
                 }
             }
         }
