@@ -23,6 +23,8 @@ namespace {
 constexpr int kBaseLds = 16384;  // ints of scanned bases kept in LDS (64 KB)
 constexpr int kPer = 4;           // elements per lane per round of loads (per-expert scans)
 constexpr int kScatterPer = 16;   // assignments per thread per round of loads (scatter)
+constexpr int kCopyPer = 8;       // counts per thread per round of loads (copy into LDS)
+constexpr int kShortRow = 8;      // rows of at most this many token blocks: one thread per expert
 
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 #pragma unroll
@@ -40,7 +42,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
                                                           int32_t* __restrict__ inv, Tile* __restrict__ tiles,
                                                           int32_t* __restrict__ n_tiles, int max_tiles, WorkList w0,
-                                                          WorkList w1, int32_t* __restrict__ zero, int n_zero) {
+                                                          WorkList w1, int32_t* __restrict__ zero, int n_zero,
+                                                          bool scatter_outside) {
     __shared__ int32_t totals[1024];
     // the scanned per-block bases, kept here when they fit (E * nblk <= kBaseLds)
     __shared__ int32_t base_lds[kBaseLds];
@@ -59,7 +62,41 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     // 1. per expert: exclusive scan of its tile counts (in place) and its total.
     //    A lane owns kPer consecutive blocks, so a row of up to 64 * kPer
     //    counts is read in one round of loads; longer rows take more rounds.
+    //    When the counts fit in LDS they are first copied there by all
+    //    threads in a few rounds of independent loads (one wave walking its
+    //    experts through global memory would wait out one load latency per
+    //    expert), and the scans read LDS.
     const bool in_lds = E * nblk <= kBaseLds;
+    if (in_lds) {
+        const int n = E * nblk;
+        for (int i0 = tid; i0 < n; i0 += 1024 * kCopyPer) {
+            int v[kCopyPer];
+#pragma unroll
+            for (int j = 0; j < kCopyPer; ++j) {
+                const int i = i0 + j * 1024;
+                v[j] = i < n ? blk[i] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < kCopyPer; ++j) {
+                const int i = i0 + j * 1024;
+                if (i < n) base_lds[i] = v[j];
+            }
+        }
+        __syncthreads();
+    }
+    if (in_lds && nblk <= kShortRow) {
+        // short rows (few token blocks): one thread per expert
+        for (int e = tid; e < E; e += 1024) {
+            int running = 0;
+            for (int b = 0; b < nblk; ++b) {
+                const int c = base_lds[e * nblk + b];
+                base_lds[e * nblk + b] = running;
+                blk[(size_t)e * nblk + b] = running;
+                running += c;
+            }
+            totals[e] = running;
+        }
+    } else
     for (int e = wave; e < E; e += 16) {
         int running = 0;
         int32_t* row = blk + (size_t)e * nblk;
@@ -68,7 +105,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
 #pragma unroll
             for (int j = 0; j < kPer; ++j) {
                 const int i = b0 + lane * kPer + j;
-                c[j] = i < nblk ? row[i] : 0;
+                c[j] = i < nblk ? (in_lds ? base_lds[e * nblk + i] : row[i]) : 0;
             }
             int sum = 0;
 #pragma unroll
@@ -203,7 +240,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     }
 
     // 4. stable scatter: row = offsets[e] + (earlier tiles' count) + rank in tile.
-    //    Loads of kScatterPer assignments are issued together.
+    //    Loads of kScatterPer assignments are issued together.  Large
+    //    batches scatter in their own launch over many CUs instead (one CU's
+    //    loads in flight would take a few dozen round trips).
+    if (scatter_outside) return;
     const int total = T * k;
     for (int a0 = 0; a0 < total; a0 += 1024 * kScatterPer) {
         int e[kScatterPer], lr[kScatterPer];
@@ -227,14 +267,41 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     }
 }
 
+// Step 4 of the route scan for large batches, one assignment per thread:
+// the same row formula, with the per-block bases from global memory.
+__global__ __launch_bounds__(256) void route_scatter_kernel(int total, int k, int nblk,
+                                                            const int32_t* __restrict__ topk_idx,
+                                                            const int32_t* __restrict__ bases,
+                                                            const int32_t* __restrict__ local_rank,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ perm_src, int32_t* __restrict__ inv) {
+    const int a = blockIdx.x * 256 + threadIdx.x;
+    if (a >= total) return;
+    const int e = topk_idx[a];
+    const int b = (a / k) / kRouterTokens;
+    const int r = offsets[e] + bases[(size_t)e * nblk + b] + local_rank[a];
+    perm_src[r] = a;
+    inv[a] = r;
+}
+
+// Batches of more assignments than this scatter in their own launch.
+constexpr int kScatterInKernelMax = 4096;
+
 }  // namespace
 
 hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx, int32_t* blk_counts,
                              const int32_t* local_rank, int32_t* offsets, int32_t* perm_src, int32_t* inv,
                              Tile* tiles, int32_t* n_tiles, int max_tiles, WorkList w0, WorkList w1, int32_t* zero,
                              int n_zero, hipStream_t stream) {
+    const int total = T * k;
+    const bool outside = total > kScatterInKernelMax;
     route_scan_kernel<<<1, 1024, 0, stream>>>(T, E, k, BM, topk_idx, blk_counts, local_rank, offsets, perm_src, inv,
-                                              tiles, n_tiles, max_tiles, w0, w1, zero, n_zero);
+                                              tiles, n_tiles, max_tiles, w0, w1, zero, n_zero, outside);
+    if (outside) {
+        const int nblk = (T + kRouterTokens - 1) / kRouterTokens;
+        route_scatter_kernel<<<(total + 255) / 256, 256, 0, stream>>>(total, k, nblk, topk_idx, blk_counts,
+                                                                      local_rank, offsets, perm_src, inv);
+    }
     return hipGetLastError();
 }
 
