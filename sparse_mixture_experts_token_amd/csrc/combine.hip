@@ -13,6 +13,8 @@
 namespace moe {
 namespace {
 
+constexpr int kSlotBatch = 8;  // slot rows whose loads are in flight together
+
 template <bool kBf16Out>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, void* __restrict__ out, int T,
                                                       int H, int k, const void* __restrict__ residual) {
@@ -22,13 +24,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         const size_t t = i / h4;
         const size_t c = i % h4;
         const float4* src = reinterpret_cast<const float4*>(y) + (t * k) * h4 + c;
-        float4 acc = src[0];
-        for (int s = 1; s < k; ++s) {
-            const float4 v = src[(size_t)s * h4];
-            acc.x += v.x;
-            acc.y += v.y;
-            acc.z += v.z;
-            acc.w += v.w;
+        // slots in batches of kSlotBatch loads issued together, added in slot order
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s0 = 0; s0 < k; s0 += kSlotBatch) {
+            float4 v[kSlotBatch];
+#pragma unroll
+            for (int j = 0; j < kSlotBatch; ++j)
+                if (s0 + j < k) v[j] = src[(size_t)(s0 + j) * h4];
+#pragma unroll
+            for (int j = 0; j < kSlotBatch; ++j) {
+                if (s0 + j >= k) break;
+                if (s0 + j == 0) {
+                    acc = v[0];
+                } else {
+                    acc.x += v[j].x;
+                    acc.y += v[j].y;
+                    acc.z += v[j].z;
+                    acc.w += v[j].w;
+                }
+            }
         }
         if (residual) {
             if constexpr (kBf16Out) {

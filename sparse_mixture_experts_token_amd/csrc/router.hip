@@ -27,6 +27,7 @@ constexpr int BT = kRouterTokens;  // tokens per workgroup
 constexpr int NW = 16;             // waves per workgroup
 constexpr int kThreads = NW * 64;
 constexpr int kCBMax = 4;          // 16-wide expert column blocks per pass (at most)
+constexpr int kPartPer = 4;        // partial-logit elements per thread per round of loads
 
 struct RouterSmem {
     // layout offsets (bytes) for a given padded expert count
@@ -178,15 +179,31 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
     const int ncb = (E + 15) >> 4;
 
     if (lpart) {
-        // the slice sums written by the small-batch logits kernel, in slice order, then the bias
-        for (int i = tid; i < BT * E; i += kThreads) {
-            const int row = i / E, e = i - row * E, t = t0 + row;
-            if (t < T) {
-                float v = 0.f;
+        // the slice sums written by the small-batch logits kernel, in slice
+        // order, then the bias (parked in LDS first); the loads of kPartPer
+        // elements are issued together
+        for (int e = tid; e < E; e += kThreads) s_bias[e] = br ? load_scalar(br, e) : 0.f;
+        __syncthreads();
+        for (int i0 = tid; i0 < BT * E; i0 += kThreads * kPartPer) {
+            float pv[kPartPer][kLogitSlices];
 #pragma unroll
-                for (int ks = 0; ks < kLogitSlices; ++ks) v += lpart[((size_t)ks * T + t) * E + e];
-                if (br) v += load_scalar(br, e);
-                s_lds[row * Ep + e] = v;
+            for (int j = 0; j < kPartPer; ++j) {
+                const int i = i0 + j * kThreads;
+                const int row = i / E, e = i - row * E, t = t0 + row;
+                const bool ok = i < BT * E && t < T;
+#pragma unroll
+                for (int ks = 0; ks < kLogitSlices; ++ks) pv[j][ks] = ok ? lpart[((size_t)ks * T + t) * E + e] : 0.f;
+            }
+#pragma unroll
+            for (int j = 0; j < kPartPer; ++j) {
+                const int i = i0 + j * kThreads;
+                const int row = i / E, e = i - row * E, t = t0 + row;
+                if (i < BT * E && t < T) {
+                    float v = 0.f;
+#pragma unroll
+                    for (int ks = 0; ks < kLogitSlices; ++ks) v += pv[j][ks];
+                    s_lds[row * Ep + e] = br ? v + s_bias[e] : v;
+                }
             }
         }
         __syncthreads();
