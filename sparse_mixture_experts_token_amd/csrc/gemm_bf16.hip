@@ -7,12 +7,13 @@
 //   down:     y[a, :]   = p_a * (act[r, :] W_down[e]^T),            a = perm_src[r]
 //
 // Workgroup tile: BM = 256 rows of one expert x BN weight rows per matrix
-// (gate/up: 128 of gate and the same 128 of up; down: 256 of W_down), eight
+// (gate/up: 128 of gate and the same 128 of up; down: 320 of W_down, 256 for
+// MXFP4 weights), eight
 // waves in a 4 x 2 layout, two per SIMD, so that one wave's MFMAs cover the
 // other's LDS and DMA issue.  Wave (wm, wn) owns the 32-row groups wm and
 // wm + 4 and half of the tile's weight rows of every matrix, as 32x32x16 bf16
 // MFMA tiles with fp32 accumulators (gate/up: 2 x 2 of gate and 2 x 2 of up,
-// so SiLU*up is formed in registers; down: 2 x 4).
+// so SiLU*up is formed in registers; down: 2 x 5, MXFP4 2 x 4).
 //
 // Operands reach LDS by buffer-to-LDS DMA.  What limits such a kernel on this
 // hardware is how many cache lines one load instruction touches: 64 lanes x
@@ -64,7 +65,11 @@ constexpr int kBK = 64;      // K per LDS stage: 128 bytes of each row
 constexpr int kXcds = 8;
 static_assert(kXcds == kXcdRanges, "the route scan cuts one work range per XCD");
 constexpr int kBNGateUp = 128;
-constexpr int kBNDown = 256;
+// Down tile width: 320 rows of W_down for bf16 weights (2880 = 9 x 320, no
+// padded last tile, and 15% fewer operand bytes per FLOP than 256), 256 for
+// MXFP4 (its 32-row code blocks must split evenly over the eight waves).
+template <bool MXW>
+constexpr int kBNDown = MXW ? 256 : 320;
 constexpr int kStagesGateUp = 2;  // 64 KB stages
 constexpr int kStagesDown = 2;    // 64 KB stages
 
@@ -634,7 +639,7 @@ __device__ __forceinline__ void gemm_body(const BArgs& args) {
 template <bool MXW>
 using CfgGateUp = Cfg<0, kBNGateUp, MXW ? 3 : kStagesGateUp, MXW>;
 template <bool MXW>
-using CfgDown = Cfg<1, kBNDown, MXW ? 3 : kStagesDown, MXW>;
+using CfgDown = Cfg<1, kBNDown<MXW>, MXW ? 3 : kStagesDown, MXW>;
 
 template <bool MXW>
 __global__ __launch_bounds__(kThreads) void gateup_bf16_kernel(BArgs args) {
@@ -642,7 +647,7 @@ __global__ __launch_bounds__(kThreads) void gateup_bf16_kernel(BArgs args) {
 }
 template <bool MXW>
 __global__ __launch_bounds__(kThreads) void down_bf16_kernel(BArgs args) {
-    gemm_body<1, kBNDown, CfgDown<MXW>::NST, MXW>(args);
+    gemm_body<1, kBNDown<MXW>, CfgDown<MXW>::NST, MXW>(args);
 }
 
 BArgs make_args(const GemmProblem& p, int mode) {
@@ -680,7 +685,7 @@ BArgs make_args(const GemmProblem& p, int mode) {
         a.n_work = p.n_work_down;
         a.bounds = p.bounds_down;
         a.queue = p.queues + kXcds;
-        a.n_ntiles = (p.H + kBNDown - 1) / kBNDown;
+        a.n_ntiles = bf16_col_tiles(p.H, 1, p.expert_dtype);
     }
     a.max_work = p.max_tiles * a.n_ntiles;
     return a;
@@ -709,7 +714,10 @@ hipError_t launch(Kern kern, size_t smem, const BArgs& a, hipStream_t stream) {
 }  // namespace
 
 int bf16_block_m() { return kBM; }
-int bf16_col_tiles(int N, int mode) { return (N + (mode == 0 ? kBNGateUp : kBNDown) - 1) / (mode == 0 ? kBNGateUp : kBNDown); }
+int bf16_col_tiles(int N, int mode, int expert_dtype) {
+    const int bn = mode == 0 ? kBNGateUp : expert_dtype == DT_MXFP4 ? kBNDown<true> : kBNDown<false>;
+    return (N + bn - 1) / bn;
+}
 
 // Dynamic LDS a workgroup may use: 160 KB less room for the static work-item slot.
 constexpr size_t kMaxLds = 160 * 1024 - 1024;
@@ -718,7 +726,7 @@ constexpr size_t kMaxLds = 160 * 1024 - 1024;
 // of K sit in LDS beside the ring), a multiple of 64.
 int mxfp4_max_k() {
     const size_t fixed = CfgGateUp<true>::SMEM > CfgDown<true>::SMEM ? CfgGateUp<true>::SMEM : CfgDown<true>::SMEM;
-    const size_t rows = 2 * kBNGateUp > kBNDown ? 2 * kBNGateUp : kBNDown;
+    const size_t rows = 2 * kBNGateUp > kBNDown<true> ? 2 * kBNGateUp : kBNDown<true>;
     return (int)((kMaxLds - fixed) / rows * 32) / 64 * 64;
 }
 

@@ -104,8 +104,8 @@ Layout layout(const moe_problem* p, int router_dt = -1, bool all_plogits = false
     // column tiles of the prefill work lists (the decode kernels need none)
     // (only the bf16-activation prefill kernels walk work lists)
     L.lists = !L.decode && p->act_dtype == MOE_BF16;
-    L.nc0 = L.lists ? moe::bf16_col_tiles(p->I, 0) : 0;
-    L.nc1 = L.lists ? moe::bf16_col_tiles(p->H, 1) : 0;
+    L.nc0 = L.lists ? moe::bf16_col_tiles(p->I, 0, p->expert_dtype) : 0;
+    L.nc1 = L.lists ? moe::bf16_col_tiles(p->H, 1, p->expert_dtype) : 0;
     L.work0 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc0 * 4);
     L.work1 = o;    o = align_up(o + (size_t)L.max_tiles * L.nc1 * 4);
     L.part = o;     o = align_up(o + (L.plogits ? moe::decode_logit_part_bytes(p->T, p->E) : 0));

@@ -281,7 +281,7 @@ constexpr int kNumQueues = 16;
 int gemm_block_m(int act_dtype, int expert_dtype, int T, int k, int E);
 // bf16-weight prefill kernels (gemm_bf16.hip)
 int bf16_block_m();
-int bf16_col_tiles(int N, int mode);
+int bf16_col_tiles(int N, int mode, int expert_dtype);  // column tiles of the gate/up (0) or down (1) work list
 hipError_t launch_gateup_bf16w(const GemmProblem& p, hipStream_t stream);
 hipError_t launch_down_bf16w(const GemmProblem& p, hipStream_t stream);
 // Decode-sized problems (bf16 activations, on average at most one 16-row tile
