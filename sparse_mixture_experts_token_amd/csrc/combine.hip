@@ -13,9 +13,9 @@
 namespace moe {
 namespace {
 
-constexpr int kSlotBatch = 8;  // slot rows whose loads are in flight together
-
-template <bool kBf16Out>
+// kSlotBatch: slot rows whose loads are in flight together (8 up to top-8;
+// 24 beyond, so a decode-sized top-20 call waits for memory once per thread)
+template <bool kBf16Out, int kSlotBatch>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, void* __restrict__ out, int T,
                                                       int H, int k, const void* __restrict__ residual) {
     const int h4 = H >> 2;
@@ -76,10 +76,13 @@ hipError_t launch_combine(int act_dtype, const float* y, void* out, int T, int H
                           hipStream_t stream) {
     const size_t n4 = (size_t)T * (H / 4);
     const int blocks = (int)((n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192);
-    if (act_dtype == DT_BF16)
-        combine_kernel<true><<<blocks, 256, 0, stream>>>(y, out, T, H, k, residual);
-    else
-        combine_kernel<false><<<blocks, 256, 0, stream>>>(y, out, T, H, k, residual);
+    if (act_dtype == DT_BF16) {
+        if (k <= 8) combine_kernel<true, 8><<<blocks, 256, 0, stream>>>(y, out, T, H, k, residual);
+        else combine_kernel<true, 24><<<blocks, 256, 0, stream>>>(y, out, T, H, k, residual);
+    } else {
+        if (k <= 8) combine_kernel<false, 8><<<blocks, 256, 0, stream>>>(y, out, T, H, k, residual);
+        else combine_kernel<false, 24><<<blocks, 256, 0, stream>>>(y, out, T, H, k, residual);
+    }
     return hipGetLastError();
 }
 

@@ -22,27 +22,23 @@
 // q = l/16) reads K elements 128g + 32j + 8q .. +7), so one instruction reads
 // 64 contiguous bytes of each of 16 weight rows; at this size every
 // per-instruction row segment from 64 to 256 bytes streams at the same rate.
-// For MXFP4 a lane reads the 32 codes [128g + 32q, 128g + 32q + 32) of its
-// row in one 16-byte load plus exactly one E8M0 scale, and feeds them to the
-// four steps as elements 8j..8j+7; a contraction is unchanged by a
-// permutation of K applied to both operands, so the activation operand is
-// read in the same permuted order.  Two consecutive MXFP4 steps read the two
-// halves of the same 128-byte line of each weight row: their loads go out as
-// adjacent instructions, in pairs of steps, which lets the L1 merge them
-// (issued a step apart they went to L2 as separate requests).  All loads of
-// a K step are issued before its MFMAs (scheduling barriers keep the
-// compiler from interleaving them, which would leave only a few loads in
-// flight); the bf16 down product keeps the next step's loads in flight while
-// multiplying, the MXFP4 kernels the second step of a pair while they
-// multiply the first.
+// For MXFP4 a lane takes the 32 codes [128g + 32q, 128g + 32q + 32) of its
+// row (16 bytes) and their one E8M0 scale, and feeds them to the four steps
+// as elements 8j..8j+7; a contraction is unchanged by a permutation of K
+// applied to both operands, so the activation operand is read in the same
+// permuted order.  The MXFP4 block kernels copy the codes into LDS a whole
+// 128-byte line per weight row at a time (see decode_pass_lds) and keep the
+// block's scales in LDS for the whole contraction.  All loads of a K step
+// are issued before its MFMAs (scheduling barriers keep the compiler from
+// interleaving them, which would leave only a few loads in flight); the
+// block kernels keep the next step's loads in flight while multiplying.
 //
 // Work split.  bf16 gate/up runs with one workgroup per CU: the (tile, weight
 // row) pairs are split into equal contiguous ranges, one per workgroup, and
 // each range into equal sub-ranges, one per wave, with boundaries on
 // multiples of four rows; a wave walks its sub-range in passes of at most 32
 // rows.  Down (64-row blocks) and MXFP4 gate/up (32-row blocks) run one block
-// per wave, in one-wave workgroups, with the next K step's loads in flight
-// (measured faster for these).
+// per wave, in one-wave workgroups (measured faster for these).
 //
 // Fused routing.  When the batch and the router are small (T <= 64, E <= 64)
 // a small kernel writes partial router logits (K split into slices), and
@@ -106,9 +102,7 @@ struct Batch {
     u32x4 b[4];
 };
 
-// With SL the MXFP4 scales are not loaded here: scales_fetch() reads them from
-// the copy scales_dma() put in LDS.
-template <int MODE, int WDT, int NP, bool SL = false>
+template <int MODE, int WDT, int NP>
 __device__ __forceinline__ void issue(Batch<MODE, WDT, NP>& x, buf_rsrc w0, buf_rsrc w1, buf_rsrc s0, buf_rsrc s1,
                                       buf_rsrc bsrc, const uint32_t (&n)[NP], const bool (&nv)[NP],
                                       uint32_t b_base, bool has_row, uint32_t K, uint32_t g, uint32_t qd) {
@@ -119,10 +113,10 @@ __device__ __forceinline__ void issue(Batch<MODE, WDT, NP>& x, buf_rsrc w0, buf_
             const bool kv = nv[p] && kq < K;
             const uint32_t co = kv ? n[p] * (K / 2) + kq / 2 : kOob, so = kv ? n[p] * (K / 32) + kq / 32 : kOob;
             x.wq[p] = buf_load16(w0, co, 0);
-            if constexpr (!SL) x.ws[p] = buf_load1(s0, so, 0);
+            x.ws[p] = buf_load1(s0, so, 0);
             if constexpr (MODE == 0) {
                 x.uq[p] = buf_load16(w1, co, 0);
-                if constexpr (!SL) x.us[p] = buf_load1(s1, so, 0);
+                x.us[p] = buf_load1(s1, so, 0);
             }
         } else {
 #pragma unroll
@@ -135,29 +129,6 @@ __device__ __forceinline__ void issue(Batch<MODE, WDT, NP>& x, buf_rsrc w0, buf_
         }
     }
     load_b<WDT>(bsrc, b_base, has_row, K, g, qd, x.b);
-}
-
-// MXFP4, staged scales: steps g and g+1 (g even) read the two halves of the
-// same 128-byte line of every weight row; their loads go out adjacent.
-template <int MODE, int NP>
-__device__ __forceinline__ void issue_pair(Batch<MODE, DT_MXFP4, NP>& x, Batch<MODE, DT_MXFP4, NP>& y, buf_rsrc w0,
-                                           buf_rsrc w1, buf_rsrc bsrc, const uint32_t (&n)[NP],
-                                           const bool (&nv)[NP], uint32_t b_base, bool has_row, uint32_t K,
-                                           uint32_t g, uint32_t qd) {
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const uint32_t kq0 = g * 128 + qd * 32, kq1 = kq0 + 128;
-        const uint32_t c0 = (nv[p] && kq0 < K) ? n[p] * (K / 2) + kq0 / 2 : kOob;
-        const uint32_t c1 = (nv[p] && kq1 < K) ? n[p] * (K / 2) + kq1 / 2 : kOob;
-        x.wq[p] = buf_load16(w0, c0, 0);
-        y.wq[p] = buf_load16(w0, c1, 0);
-        if constexpr (MODE == 0) {
-            x.uq[p] = buf_load16(w1, c0, 0);
-            y.uq[p] = buf_load16(w1, c1, 0);
-        }
-    }
-    load_b<DT_MXFP4>(bsrc, b_base, has_row, K, g, qd, x.b);
-    load_b<DT_MXFP4>(bsrc, b_base, has_row, K, g + 1, qd, y.b);
 }
 
 template <int PATH, int NQ>
@@ -262,13 +233,47 @@ __device__ __forceinline__ void scales_fetch(Batch<MODE, WDT, NP>& x, const uint
     }
 }
 
+// Epilogue of a block.  D: lane l holds weight rows 4(l/16)+i (i = 0..3) of
+// the panel, for row l%16 of the tile; c0 and c1 are multiples of four, so
+// those four rows are all present or all absent.
+template <int MODE, int NP>
+__device__ __forceinline__ void store_block(const DArgs& a, const f32x4 (&acc0)[NP], const f32x4 (&acc1)[NP],
+                                            const int32_t* perm, int row0, int r, uint32_t qd, bool has_row,
+                                            uint32_t c0, uint32_t c1) {
+    const uint32_t N = (uint32_t)a.N;
+    if (!has_row) return;
+    if constexpr (MODE == 0) {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (size_t)(row0 + r) * N;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const uint32_t n0 = c0 + (uint32_t)(p * 16) + 4 * qd;
+            if (n0 >= c1) continue;
+            uint32_t v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16_bits(silu_f(acc0[p][i]) * acc1[p][i]);
+            *reinterpret_cast<uint2*>(orow + n0) = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+        }
+    } else {
+        const int asg = perm[row0 + r];
+        const float pw = a.topk_w[asg];
+        float* orow = reinterpret_cast<float*>(a.out) + (size_t)asg * N;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const uint32_t n0 = c0 + (uint32_t)(p * 16) + 4 * qd;
+            if (n0 >= c1) continue;
+            *reinterpret_cast<float4*>(orow + n0) =
+                float4{acc0[p][0] * pw, acc0[p][1] * pw, acc0[p][2] * pw, acc0[p][3] * pw};
+        }
+    }
+}
+
 // One block: weight rows [c0, c1) (c1 - c0 <= 16 NP, both multiples of four)
 // of the expert of `tile` against the tile's activation rows; perm holds the
 // assignment of every expert-major row (global memory or LDS).  DEPTH = K
 // steps of loads in flight (1 or 2).
-template <int MODE, int WDT, int DEPTH, int NP = kPanels, bool SL = false>
+template <int MODE, int WDT, int DEPTH, int NP = kPanels>
 __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, const int32_t* perm, uint32_t c0,
-                                            uint32_t c1, int lane, uint8_t* sl = nullptr) {
+                                            uint32_t c1, int lane) {
     const int e = tile.expert, row0 = tile.row_start, rows = tile.rows;
     const uint32_t K = (uint32_t)a.K, N = (uint32_t)a.N;
     const int r = lane & 15;
@@ -311,34 +316,7 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
     // Steps past the end read beyond K: zeros, no memory traffic.
     const uint32_t ng = (K + 127) / 128;
     Batch<MODE, WDT, NP> x0, x1;
-    constexpr bool kSL = SL && WDT == DT_MXFP4;
-    const uint32_t KG = K / 32;
-    if constexpr (kSL) {
-        // scales of the whole block into LDS; their loads go out first and the
-        // first K step's code loads overlap their latency
-        static_assert(DEPTH == 2, "staged scales: two K steps in flight");
-        constexpr int NMAT = MODE == 0 ? 2 : 1;
-        scales_dma<NP, NMAT>(s0, s1, c0, KG, sl, lane);
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        issue_pair<MODE, NP>(x0, x1, w0, w1, bsrc, n, nv, b_base, has_row, K, 0, qd);
-        // The compiler does not track the LDS writes of the copies above.  Loads
-        // retire in issue order; the scales went out first.
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NP * NMAT + 8) : "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        // a pair of steps per iteration; the next pair's loads go out behind
-        // this pair's MFMAs
-        for (uint32_t g = 0; g < ng; g += 2) {
-            scales_fetch<MODE, WDT, NP>(x0, sl, nv, KG, g, r, qd);
-            compute<MODE, WDT, NP, true>(x0, acc0, acc1);
-            __builtin_amdgcn_sched_barrier(0);
-            scales_fetch<MODE, WDT, NP>(x1, sl, nv, KG, g + 1, r, qd);
-            compute<MODE, WDT, NP, true>(x1, acc0, acc1);
-            __builtin_amdgcn_sched_barrier(0);
-            issue_pair<MODE, NP>(x0, x1, w0, w1, bsrc, n, nv, b_base, has_row, K, g + 2, qd);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    } else if constexpr (DEPTH == 1) {
+    if constexpr (DEPTH == 1) {
         for (uint32_t g = 0; g < ng; ++g) {
             issue<MODE, WDT, NP>(x0, w0, w1, s0, s1, bsrc, n, nv, b_base, has_row, K, g, qd);
             __builtin_amdgcn_sched_barrier(0);
@@ -359,33 +337,142 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
         }
     }
 
-    // D: lane l holds weight rows 4(l/16)+i (i = 0..3) of the panel, for row l%16
-    // of the tile; c0 and c1 are multiples of four, so those four rows are all
-    // present or all absent.
-    if (!has_row) return;
-    if constexpr (MODE == 0) {
-        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + (size_t)(row0 + r) * N;
+    store_block<MODE, NP>(a, acc0, acc1, perm, row0, r, qd, has_row, c0, c1);
+}
+
+// MXFP4 codes through LDS.  A super-step is 256 K: one whole 128-byte line of
+// every weight row of the block.  The block's 64 row lines (L = 16 (p NMAT +
+// m) + r for panel p, matrix m, row r of the panel) are copied by 8 DMA
+// instructions of 16 bytes per lane, 8 lanes per line, so every request the
+// L1 sends on is a whole line (register loads of 16 rows x 64 bytes made
+// half-line requests, and the count of requests in flight per CU is what
+// capped those kernels).  Position j of line L in LDS holds chunk j ^ ((r >> 1)
+// & 7) of the line: a K step reads 16 B at 16 rows of a panel with no bank
+// conflicts.  Step h (0, 1) of super-step s is K step g = 2 s + h, with the
+// same K order as the register path (lane quarter qd takes chunk 4 h + qd).
+constexpr int kLineRows = 64;  // row lines per super-step: 16 NP NMAT
+constexpr uint32_t kRingSlot = kLineRows * 128;
+
+template <int NP, int NMAT>
+__device__ __forceinline__ void codes_dma(buf_rsrc w0, buf_rsrc w1, const uint32_t (&lane_off)[2],
+                                          const bool (&lane_ok)[2][NP], uint32_t c0, uint32_t K, uint32_t s,
+                                          const uint32_t (&lane_k)[2], unsigned char* slot) {
+    static_assert(16 * NP * NMAT == kLineRows, "one ring slot per super-step");
+    const bool kv[2] = {256 * s + lane_k[0] < K, 256 * s + lane_k[1] < K};
+#pragma unroll
+    for (int i = 0; i < 2 * NP * NMAT; ++i) {
+        const int pm = i / 2, p = pm / NMAT, m = pm % NMAT, hh = i & 1;
+        const uint32_t o = (lane_ok[hh][p] && kv[hh]) ? (c0 + 16 * p) * (K / 2) + 128 * s + lane_off[hh] : kOob;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(m ? w1 : w0, (lds_void*)(slot + i * 1024), 16, o, 0, 0, 0);
+    }
+}
+
+template <int MODE, int NP, int D>
+__device__ __forceinline__ void decode_pass_lds(const DArgs& a, const Tile tile, const int32_t* perm, uint32_t c0,
+                                                uint32_t c1, int lane, unsigned char* lds) {
+    constexpr int NMAT = MODE == 0 ? 2 : 1;
+    static_assert(D == 2 || D == 3, "ring of two or three super-steps");
+    const int e = tile.expert, row0 = tile.row_start, rows = tile.rows;
+    const uint32_t K = (uint32_t)a.K, N = (uint32_t)a.N;
+    const int r = lane & 15;
+    const uint32_t qd = (uint32_t)(lane >> 4);
+
+    const bool has_row = r < rows;
+    uint32_t b_base = 0;
+    if (has_row) {
+        const int src = MODE == 0 ? perm[row0 + r] / a.k : row0 + r;
+        b_base = (uint32_t)src * K * 2u;
+    }
+    const buf_rsrc bsrc = make_rsrc(a.a_src, a.a_bytes);
+    bool nv[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) nv[p] = c0 + (uint32_t)(p * 16 + r) < c1;
+
+    const uint32_t wb = N * K / 2, sb = N * K / 32;
+    const buf_rsrc w0 = make_rsrc((const unsigned char*)a.w0 + (size_t)e * wb, wb);
+    const buf_rsrc s0 = make_rsrc(a.s0 + (size_t)e * sb, sb);
+    const buf_rsrc w1 = MODE == 0 ? make_rsrc((const unsigned char*)a.w1 + (size_t)e * wb, wb) : w0;
+    const buf_rsrc s1 = MODE == 0 ? make_rsrc(a.s1 + (size_t)e * sb, sb) : s0;
+
+    // DMA side: lane l of an instruction copies position l % 8 of line row
+    // 8 (i % 2) + l / 8 of its panel
+    const uint32_t pos = (uint32_t)(lane & 7);
+    uint32_t lane_off[2];
+    bool lane_ok[2][NP];
+    uint32_t lane_k[2];  // first K element of the chunk copied, within the super-step
+    {
+        const uint32_t rr0 = (uint32_t)(lane >> 3), ch0 = pos ^ ((rr0 >> 1) & 7u);
+        const uint32_t rr1 = rr0 + 8, ch1 = pos ^ ((rr1 >> 1) & 7u);
+        lane_off[0] = rr0 * (K / 2) + ch0 * 16;
+        lane_off[1] = rr1 * (K / 2) + ch1 * 16;
+        lane_k[0] = 32 * ch0;
+        lane_k[1] = 32 * ch1;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
-            const uint32_t n0 = c0 + (uint32_t)(p * 16) + 4 * qd;
-            if (n0 >= c1) continue;
-            uint32_t v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = f32_to_bf16_bits(silu_f(acc0[p][i]) * acc1[p][i]);
-            *reinterpret_cast<uint2*>(orow + n0) = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
-        }
-    } else {
-        const int asg = perm[row0 + r];
-        const float pw = a.topk_w[asg];
-        float* orow = reinterpret_cast<float*>(a.out) + (size_t)asg * N;
-#pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            const uint32_t n0 = c0 + (uint32_t)(p * 16) + 4 * qd;
-            if (n0 >= c1) continue;
-            *reinterpret_cast<float4*>(orow + n0) =
-                float4{acc0[p][0] * pw, acc0[p][1] * pw, acc0[p][2] * pw, acc0[p][3] * pw};
+            lane_ok[0][p] = c0 + (uint32_t)(16 * p) + rr0 < c1;
+            lane_ok[1][p] = c0 + (uint32_t)(16 * p) + rr1 < c1;
         }
     }
+    // read side: this lane's row line offset and the swizzle of its row
+    const uint32_t rd_row = (uint32_t)r * 128u, rd_sw = ((uint32_t)r >> 1) & 7u;
+    unsigned char* ring = lds;
+    uint8_t* sl = lds + D * kRingSlot;
+
+    f32x4 acc0[NP], acc1[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) acc0[p] = acc1[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t KG = K / 32, ns = (K + 255) / 256;
+    u32x4 bq[2][2][4];  // activations of super-steps s and s+1 (two K steps each)
+
+    // issue order: scales, codes C_0 .. C_{D-2}, activations B_0; super-step s
+    // issues C_{s+D-1}, then B_{s+1}, after which B_s, C_s and all before them
+    // are all but the last 16 loads issued
+    scales_dma<NP, NMAT>(s0, s1, c0, KG, sl, lane);
+#pragma unroll
+    for (int i = 0; i + 1 < D; ++i)
+        codes_dma<NP, NMAT>(w0, w1, lane_off, lane_ok, c0, K, (uint32_t)i, lane_k, ring + i * kRingSlot);
+    load_b<DT_MXFP4>(bsrc, b_base, has_row, K, 0, qd, bq[0][0]);
+    load_b<DT_MXFP4>(bsrc, b_base, has_row, K, 1, qd, bq[0][1]);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+
+    auto step = [&](uint32_t s, int cur) {
+        const uint32_t sn = s + (uint32_t)(D - 1);
+        codes_dma<NP, NMAT>(w0, w1, lane_off, lane_ok, c0, K, sn, lane_k, ring + (sn % D) * kRingSlot);
+        load_b<DT_MXFP4>(bsrc, b_base, has_row, K, 2 * (s + 1), qd, bq[cur ^ 1][0]);
+        load_b<DT_MXFP4>(bsrc, b_base, has_row, K, 2 * (s + 1) + 1, qd, bq[cur ^ 1][1]);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        const unsigned char* slot = ring + (s % D) * kRingSlot;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t g = 2 * s + (uint32_t)h;  // past K: codes, scales and activations read as zeros
+            Batch<MODE, DT_MXFP4, NP> x;
+            const uint32_t cpos = ((4u * (uint32_t)h + qd) ^ rd_sw) * 16u;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                x.wq[p] = *reinterpret_cast<const u32x4*>(slot + (p * NMAT) * 2048 + rd_row + cpos);
+                if constexpr (MODE == 0)
+                    x.uq[p] = *reinterpret_cast<const u32x4*>(slot + (p * NMAT + 1) * 2048 + rd_row + cpos);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) x.b[j] = bq[cur][h][j];
+            scales_fetch<MODE, DT_MXFP4, NP>(x, sl, nv, KG, g, r, qd);
+            compute<MODE, DT_MXFP4, NP, true>(x, acc0, acc1);
+        }
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // pairs of super-steps (the activation registers alternate); an odd count
+    // ends with a super-step past K, all zeros
+    for (uint32_t s = 0; s < ns; s += 2) {
+        step(s, 0);
+        step(s + 1, 1);
+    }
+    // the copies still in flight read past K (zeros, no memory traffic) but
+    // write this wave's LDS: let them land before the wave ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    store_block<MODE, NP>(a, acc0, acc1, perm, row0, r, qd, has_row, c0, c1);
 }
 
 // This wave's equal share of the (tile, weight row) pairs, tile-major, in
@@ -421,9 +508,9 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_balanced_kernel(DArgs a)
 }
 
 // One block of 16 NP weight rows per wave: wave q takes block q % nb of tile
-// q / nb, nb = ceil(N / (16 NP)).  SL: MXFP4 scales staged in LDS (K/32 <= kScaleMaxKg).
-template <int MODE, int WDT, int DEPTH, int NP, bool SL>
-__device__ __forceinline__ void decode_block_body(const DArgs& a) {
+// q / nb, nb = ceil(N / (16 NP)).
+template <int MODE, int WDT, int DEPTH, int NP>
+__global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int ntl = min(a.n_tiles[0], a.max_tiles);
     constexpr uint32_t kRows = 16 * NP;
@@ -432,23 +519,23 @@ __device__ __forceinline__ void decode_block_body(const DArgs& a) {
     const int mt = q / ncb, cb = q - mt * ncb;
     if (mt >= ntl) return;  // wave-uniform; this kernel has no barriers
     const uint32_t c0 = (uint32_t)cb * kRows;
-    extern __shared__ __align__(16) unsigned char dsm[];  // SL: the block's scales (one wave per workgroup)
-    static_assert(!SL || kBlkWaves == 1, "staged scales are per wave");
-    decode_pass<MODE, WDT, DEPTH, NP, SL>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane,
-                                          dsm);
+    decode_pass<MODE, WDT, DEPTH, NP>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane);
 }
 
-template <int MODE, int WDT, int DEPTH, int NP, bool SL>
-__global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
-    decode_block_body<MODE, WDT, DEPTH, NP, SL>(a);
-}
-
-// MXFP4: registers capped for three waves per SIMD (the loads in flight are
-// what the kernel's speed rests on).
-template <int MODE, int DEPTH, int NP>
-__global__ __launch_bounds__(kBlkWaves * 64) __attribute__((amdgpu_waves_per_eu(3))) void decode_block_mx_kernel(
-    DArgs a) {
-    decode_block_body<MODE, DT_MXFP4, DEPTH, NP, true>(a);
+// MXFP4, codes through LDS: one block per one-wave workgroup (the same split
+// of blocks); the LDS (D ring slots and the scales) caps the waves per CU.
+template <int MODE, int NP, int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void decode_block_mxl_kernel(DArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int ntl = min(a.n_tiles[0], a.max_tiles);
+    constexpr uint32_t kRows = 16 * NP;
+    const int ncb = (int)(((uint32_t)a.N + kRows - 1) / kRows);
+    const int q = blockIdx.x;
+    const int mt = q / ncb, cb = q - mt * ncb;
+    if (mt >= ntl) return;
+    const uint32_t c0 = (uint32_t)cb * kRows;
+    extern __shared__ __align__(16) unsigned char dsm[];
+    decode_pass_lds<MODE, NP, D>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane, dsm);
 }
 
 // ------------------------------------------------ fused routing + gate/up --
@@ -775,6 +862,7 @@ int cu_count() {
 }
 
 constexpr int kMaxLds = 160 * 1024;
+constexpr int kMxRing = 2;  // MXFP4 decode: LDS ring slots (super-steps) for the codes
 
 template <auto Kern>
 hipError_t allow_lds() {
@@ -786,13 +874,15 @@ hipError_t launch_blocks(const GemmProblem& p, hipStream_t stream) {
     const DArgs a = make_dargs(p, MODE);
     const size_t ncb = ((size_t)a.N + 16 * NP - 1) / (16 * NP);
     const int blocks = (int)(((size_t)p.max_tiles * ncb + kBlkWaves - 1) / kBlkWaves);
-    // MXFP4: the block's scales in LDS, [panel][matrix][16][K/32] bytes
-    constexpr bool kSL = WDT == DT_MXFP4;
-    static_assert(!kSL || DEPTH == 2, "staged scales: two K steps in flight");
-    if (kSL && (uint32_t)a.K / 32 > kScaleMaxKg) return hipErrorInvalidValue;  // beyond the MXFP4 K limit
-    const size_t smem = kSL ? (size_t)NP * (MODE == 0 ? 2 : 1) * scale_lines(a.K / 32) * 256 : 0;
-    if constexpr (kSL) decode_block_mx_kernel<MODE, DEPTH, NP><<<blocks, kBlkWaves * 64, smem, stream>>>(a);
-    else decode_block_kernel<MODE, WDT, DEPTH, NP, false><<<blocks, kBlkWaves * 64, smem, stream>>>(a);
+    if constexpr (WDT == DT_MXFP4) {
+        // LDS: the codes' ring, then the block's scales, [panel][matrix][16][K/32] bytes
+        static_assert(kBlkWaves == 1, "one block per workgroup");
+        if ((uint32_t)a.K / 32 > kScaleMaxKg) return hipErrorInvalidValue;  // beyond the MXFP4 K limit
+        const size_t smem = kMxRing * kRingSlot + (size_t)NP * (MODE == 0 ? 2 : 1) * scale_lines(a.K / 32) * 256;
+        decode_block_mxl_kernel<MODE, NP, kMxRing><<<blocks, 64, smem, stream>>>(a);
+    } else {
+        decode_block_kernel<MODE, WDT, DEPTH, NP><<<blocks, kBlkWaves * 64, 0, stream>>>(a);
+    }
     return hipGetLastError();
 }
 

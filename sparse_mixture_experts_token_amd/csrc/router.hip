@@ -11,7 +11,9 @@
 // sixteen partial sums are added in a fixed order, so every expert column goes
 // through exactly the same sequence of operations: two identical router rows
 // (silent copies) give bitwise-identical logits.  Top-k then takes one token
-// per wave: k rounds of a wave-wide arg-max over DPP lane moves.
+// per wave: up to 64 experts by rank (an expert is chosen when fewer than k
+// order keys beat its own), beyond that by finding the k-th largest key one
+// bit at a time with wave ballots (32 rounds, whatever k is).
 //
 // Besides topk_idx / topk_w the kernel writes, for the stable expert-major
 // permutation built by the next stage:
@@ -53,36 +55,7 @@ __device__ __forceinline__ float load_scalar<float>(const float* p, size_t i) { 
 template <>
 __device__ __forceinline__ float load_scalar<uint16_t>(const uint16_t* p, size_t i) { return bf16_bits_to_f32(p[i]); }
 
-constexpr int kNone = 0x7fffffff;
-
-// (value, index) order: larger value wins, then lower index.  A lane without
-// a candidate holds index kNone; any candidate beats it, so a candidate is
-// always found while one exists (even for NaN or -inf logits).
-__device__ __forceinline__ void argmax_merge(float& v, int& idx, float ov, int oi) {
-    // non-short-circuit operators: straight-line selects, no divergent branches
-    const bool take = (oi != kNone) & ((idx == kNone) | (ov > v) | ((ov == v) & (oi < idx)));
-    v = take ? ov : v;
-    idx = take ? oi : idx;
-}
-
-template <int CTRL>
-__device__ __forceinline__ void argmax_dpp(float& v, int& idx) {
-    argmax_merge(v, idx, dpp_f<CTRL>(v), dpp_i<CTRL>(idx));
-}
-
-// Wave-wide arg-max; the result is the same in every lane.
-__device__ __forceinline__ void wave_argmax(float& v, int& idx) {
-    argmax_dpp<kDppXor1>(v, idx);
-    argmax_dpp<kDppXor2>(v, idx);
-    argmax_dpp<kDppHalfMirror>(v, idx);
-    argmax_dpp<kDppMirror>(v, idx);  // every lane holds its 16-lane row's result
-    float bv = lane_f(v, 0);
-    int bi = __builtin_amdgcn_readlane(idx, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) argmax_merge(bv, bi, lane_f(v, 16 * r), __builtin_amdgcn_readlane(idx, 16 * r));
-    v = bv;
-    idx = bi;
-}
+__device__ __forceinline__ uint32_t umax_u32(uint32_t a, uint32_t b) { return a > b ? a : b; }
 
 // One pass over K for CB 16-wide expert column blocks starting at cb0.
 // Each wave takes the 32-wide K steps wave, wave + 4, ...; the loads of P
@@ -191,8 +164,11 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
                 const int i = i0 + j * kThreads;
                 const int row = i / E, e = i - row * E, t = t0 + row;
                 const bool ok = i < BT * E && t < T;
+                // an absent element reads element 0 (no branch around the loads:
+                // all of them go out before the first is used)
+                const size_t o = ok ? (size_t)t * E + e : 0;
 #pragma unroll
-                for (int ks = 0; ks < kLogitSlices; ++ks) pv[j][ks] = ok ? lpart[((size_t)ks * T + t) * E + e] : 0.f;
+                for (int ks = 0; ks < kLogitSlices; ++ks) pv[j][ks] = lpart[(size_t)ks * T * E + o];
             }
 #pragma unroll
             for (int j = 0; j < kPartPer; ++j) {
@@ -278,40 +254,66 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
             }
         }
     } else
-    // Lane owns experts e = lane + 64 i, i < NV (NV = padded E / 64).
+    // Lane owns experts e = lane + 64 i, i < NV (NV = padded E / 64).  The
+    // k-th largest value key is found one bit at a time from the top: a
+    // candidate stays when at least k keys reach it, a count that takes NV
+    // ballots.  The experts above that key are selected, and of those equal
+    // to it the lowest indices, as many as are still missing.  Steps are wave
+    // uniform and independent of k.
     for (int tt = wave; tt < BT; tt += NW) {
         const int t = t0 + tt;
         if (t >= T) break;  // wave-uniform
         float orig[NV];
-        uint32_t live = 0;  // bit i: expert lane + 64 i exists
+        uint32_t key[NV];   // value key, 0 for an absent expert (and for NaN)
+        bool live[NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int e = lane + 64 * i;
-            const bool ok = e < E;
-            orig[i] = ok ? s_lds[tt * Ep + e] : -INFINITY;
-            live |= ok ? (1u << i) : 0u;
+            live[i] = e < E;
+            orig[i] = live[i] ? s_lds[tt * Ep + e] : 0.f;
+            key[i] = live[i] ? (uint32_t)(order_key(orig[i], e) >> 32) : 0u;
         }
         if (logits_opt) {
 #pragma unroll
             for (int i = 0; i < NV; ++i)
-                if ((live >> i) & 1u) logits_opt[(size_t)t * E + lane + 64 * i] = orig[i];
+                if (live[i]) logits_opt[(size_t)t * E + lane + 64 * i] = orig[i];
         }
-        uint32_t selmask = 0;
-        float smax = 0.f;
-        for (int r = 0; r < k; ++r) {
-            float bv = -INFINITY;
-            int bi = kNone;
+        // largest tau with at least k keys >= tau (candidates are >= 1, so
+        // absent experts never count; tau = 0 leaves only NaN logits to tie)
+        uint32_t tau = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+            const uint32_t cand = tau | (1u << bit);
+            int cnt = 0;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const bool cand = ((live & ~selmask) >> i) & 1u;
-                const bool take = cand & ((bi == kNone) | (orig[i] > bv));  // ascending e: ties keep the lower index
-                bv = take ? orig[i] : bv;
-                bi = take ? lane + 64 * i : bi;
-            }
-            wave_argmax(bv, bi);
-            if (r == 0) smax = bv;
-            if (bi < E && (bi & 63) == lane) selmask |= 1u << (bi >> 6);
+            for (int i = 0; i < NV; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+            tau = cnt >= k ? cand : tau;
         }
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        int above = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) above += __popcll(__ballot(live[i] && key[i] > tau));
+        const int need = k - above;  // >= 1 ties at tau, taken in ascending expert order
+        uint32_t selmask = 0, kmax = 0;
+        int ties_before = 0;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const bool tie = live[i] && key[i] == tau;
+            const uint64_t tm = __ballot(tie);
+            const bool sel = (live[i] && key[i] > tau) || (tie && ties_before + __popcll(tm & lt) < need);
+            selmask |= sel ? (1u << i) : 0u;
+            kmax = (sel && key[i] > kmax) ? key[i] : kmax;
+            ties_before += __popcll(tm);
+        }
+        // the largest selected value (the top-1), from its key
+        kmax = umax_u32(kmax, (uint32_t)dpp_i<kDppXor1>((int)kmax));
+        kmax = umax_u32(kmax, (uint32_t)dpp_i<kDppXor2>((int)kmax));
+        kmax = umax_u32(kmax, (uint32_t)dpp_i<kDppHalfMirror>((int)kmax));
+        kmax = umax_u32(kmax, (uint32_t)dpp_i<kDppMirror>((int)kmax));
+        kmax = umax_u32(umax_u32((uint32_t)__builtin_amdgcn_readlane((int)kmax, 0),
+                                 (uint32_t)__builtin_amdgcn_readlane((int)kmax, 16)),
+                        umax_u32((uint32_t)__builtin_amdgcn_readlane((int)kmax, 32),
+                                 (uint32_t)__builtin_amdgcn_readlane((int)kmax, 48)));
+        const float smax = __uint_as_float((kmax & 0x80000000u) ? (kmax & 0x7fffffffu) : ~kmax);
         // softmax over the selected set, summed in a fixed order
         float z[NV];
         float zs = 0.f;
@@ -323,7 +325,6 @@ __global__ __launch_bounds__(kThreads) void router_kernel(const TA* __restrict__
         const float denom = wave_sum(zs);
         // position in ascending expert order
         int before = 0;
-        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const bool sel = (selmask >> i) & 1u;
