@@ -340,40 +340,48 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
     store_block<MODE, NP>(a, acc0, acc1, perm, row0, r, qd, has_row, c0, c1);
 }
 
-// MXFP4 codes through LDS.  A super-step is 256 K: one whole 128-byte line of
-// every weight row of the block.  The block's 64 row lines (L = 16 (p NMAT +
-// m) + r for panel p, matrix m, row r of the panel) are copied by 8 DMA
-// instructions of 16 bytes per lane, 8 lanes per line, so every request the
-// L1 sends on is a whole line (register loads of 16 rows x 64 bytes made
-// half-line requests, and the count of requests in flight per CU is what
-// capped those kernels).  Position j of line L in LDS holds chunk j ^ ((r >> 1)
-// & 7) of the line: a K step reads 16 B at 16 rows of a panel with no bank
-// conflicts.  Step h (0, 1) of super-step s is K step g = 2 s + h, with the
-// same K order as the register path (lane quarter qd takes chunk 4 h + qd).
-constexpr int kLineRows = 64;  // row lines per super-step: 16 NP NMAT
-constexpr uint32_t kRingSlot = kLineRows * 128;
+// MXFP4 codes through LDS.  A super-step is 256 K: 128 bytes of every weight
+// row of the block.  A row's codes start anywhere on the 128-byte line grid
+// (row n at byte n K/2 of its expert), so the copies follow the grid, not the
+// rows: line j of a row is the j-th 128-byte memory line from the one holding
+// its first code, and super-step s reads lines s and s + 1.  Every request
+// the L1 sends on is then a whole line; copying the rows' own 128-byte
+// spans, which straddle two lines, made twice the requests and ran about 10%
+// slower.  The block's 16 NP NMAT row lines (L = 16 (p NMAT + m) + r for
+// panel p, matrix m, row r of the panel) take 2 NP NMAT DMA instructions of
+// 16 bytes per lane, 8 lanes per line; a lane copies only the 16-byte units
+// inside its row (the rest read as zero, without memory traffic).  Smaller
+// blocks (16-row gate/up, 32-row down) measured slower.  Position u of line L in LDS
+// holds unit u ^ ((r >> 1) & 7) of the memory line: a K step reads 16 B at 16
+// rows of a panel with few bank conflicts.  A ring of three slots holds lines
+// s and s + 1 while line s + 2 is copied.  Step h (0, 1) of super-step s is K
+// step g = 2 s + h, with the K order of the register path (lane quarter qd
+// takes the codes of K [256 s + 32 c, + 32), c = 4 h + qd).
+constexpr int kMxRing = 3;  // ring slots (lines) for the codes
+// bytes of one ring slot: a line of each of the block's 16 NP NMAT rows
+template <int NP, int NMAT>
+constexpr uint32_t ring_slot() { return 16u * NP * NMAT * 128u; }
 
 template <int NP, int NMAT>
-__device__ __forceinline__ void codes_dma(buf_rsrc w0, buf_rsrc w1, const uint32_t (&lane_off)[2],
-                                          const bool (&lane_ok)[2][NP], uint32_t c0, uint32_t K, uint32_t s,
-                                          const uint32_t (&lane_k)[2], unsigned char* slot) {
-    static_assert(16 * NP * NMAT == kLineRows, "one ring slot per super-step");
-    const bool kv[2] = {256 * s + lane_k[0] < K, 256 * s + lane_k[1] < K};
+__device__ __forceinline__ void line_dma(buf_rsrc w0, buf_rsrc w1, const uint32_t (&row_base)[2 * NP * NMAT],
+                                         const int32_t (&rel)[2 * NP * NMAT], uint32_t half_k, uint32_t j,
+                                         unsigned char* slot) {
 #pragma unroll
     for (int i = 0; i < 2 * NP * NMAT; ++i) {
-        const int pm = i / 2, p = pm / NMAT, m = pm % NMAT, hh = i & 1;
-        const uint32_t o = (lane_ok[hh][p] && kv[hh]) ? (c0 + 16 * p) * (K / 2) + 128 * s + lane_off[hh] : kOob;
+        const int m = (i / 2) % NMAT;
+        const uint32_t t = 128u * j + (uint32_t)rel[i];  // byte of the unit within its row (unsigned: < 0 is large)
+        const uint32_t o = t < half_k ? row_base[i] + t : kOob;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(m ? w1 : w0, (lds_void*)(slot + i * 1024), 16, o, 0, 0, 0);
     }
 }
 
-template <int MODE, int NP, int D>
+template <int MODE, int NP>
 __device__ __forceinline__ void decode_pass_lds(const DArgs& a, const Tile tile, const int32_t* perm, uint32_t c0,
                                                 uint32_t c1, int lane, unsigned char* lds) {
     constexpr int NMAT = MODE == 0 ? 2 : 1;
-    static_assert(D == 2 || D == 3, "ring of two or three super-steps");
+    constexpr int D = kMxRing;
     const int e = tile.expert, row0 = tile.row_start, rows = tile.rows;
-    const uint32_t K = (uint32_t)a.K, N = (uint32_t)a.N;
+    const uint32_t K = (uint32_t)a.K, N = (uint32_t)a.N, half_k = K / 2;
     const int r = lane & 15;
     const uint32_t qd = (uint32_t)(lane >> 4);
 
@@ -388,35 +396,45 @@ __device__ __forceinline__ void decode_pass_lds(const DArgs& a, const Tile tile,
 #pragma unroll
     for (int p = 0; p < NP; ++p) nv[p] = c0 + (uint32_t)(p * 16 + r) < c1;
 
-    const uint32_t wb = N * K / 2, sb = N * K / 32;
-    const buf_rsrc w0 = make_rsrc((const unsigned char*)a.w0 + (size_t)e * wb, wb);
+    const uint32_t wb = N * half_k, sb = N * K / 32;
+    const unsigned char* wp0 = (const unsigned char*)a.w0 + (size_t)e * wb;
+    const unsigned char* wp1 = MODE == 0 ? (const unsigned char*)a.w1 + (size_t)e * wb : wp0;
+    const buf_rsrc w0 = make_rsrc(wp0, wb);
     const buf_rsrc s0 = make_rsrc(a.s0 + (size_t)e * sb, sb);
-    const buf_rsrc w1 = MODE == 0 ? make_rsrc((const unsigned char*)a.w1 + (size_t)e * wb, wb) : w0;
+    const buf_rsrc w1 = MODE == 0 ? make_rsrc(wp1, wb) : w0;
     const buf_rsrc s1 = MODE == 0 ? make_rsrc(a.s1 + (size_t)e * sb, sb) : s0;
+    // byte of the line grid where each matrix's expert block starts
+    const uint32_t grid0 = (uint32_t)reinterpret_cast<uintptr_t>(wp0) & 127u;
+    const uint32_t grid1 = (uint32_t)reinterpret_cast<uintptr_t>(wp1) & 127u;
 
-    // DMA side: lane l of an instruction copies position l % 8 of line row
-    // 8 (i % 2) + l / 8 of its panel
-    const uint32_t pos = (uint32_t)(lane & 7);
-    uint32_t lane_off[2];
-    bool lane_ok[2][NP];
-    uint32_t lane_k[2];  // first K element of the chunk copied, within the super-step
+    // DMA side: instruction i = 2 (p NMAT + m) + hh; lane l copies position
+    // l % 8 of the line of row 8 hh + l / 8 of panel p, matrix m
+    uint32_t row_base[2 * NP * NMAT];
+    int32_t rel[2 * NP * NMAT];
     {
-        const uint32_t rr0 = (uint32_t)(lane >> 3), ch0 = pos ^ ((rr0 >> 1) & 7u);
-        const uint32_t rr1 = rr0 + 8, ch1 = pos ^ ((rr1 >> 1) & 7u);
-        lane_off[0] = rr0 * (K / 2) + ch0 * 16;
-        lane_off[1] = rr1 * (K / 2) + ch1 * 16;
-        lane_k[0] = 32 * ch0;
-        lane_k[1] = 32 * ch1;
+        const uint32_t pos = (uint32_t)(lane & 7);
 #pragma unroll
-        for (int p = 0; p < NP; ++p) {
-            lane_ok[0][p] = c0 + (uint32_t)(16 * p) + rr0 < c1;
-            lane_ok[1][p] = c0 + (uint32_t)(16 * p) + rr1 < c1;
+        for (int i = 0; i < 2 * NP * NMAT; ++i) {
+            const int pm = i / 2, p = pm / NMAT, m = pm % NMAT;
+            const uint32_t rr = (uint32_t)(lane >> 3) + 8u * (uint32_t)(i & 1);
+            const uint32_t n = c0 + 16u * (uint32_t)p + rr;
+            const uint32_t off = ((m ? grid1 : grid0) + n * half_k) & 127u;  // first code's byte in its line
+            const uint32_t u = pos ^ ((rr >> 1) & 7u);
+            row_base[i] = n < c1 ? n * half_k : kOob;
+            rel[i] = (int32_t)(16u * u) - (int32_t)off;
         }
     }
-    // read side: this lane's row line offset and the swizzle of its row
+    // read side: the line position of this lane's rows' first codes, in 16-byte units
+    uint32_t rd_o[NP * NMAT];
+#pragma unroll
+    for (int pm = 0; pm < NP * NMAT; ++pm) {
+        const uint32_t n = c0 + 16u * (uint32_t)(pm / NMAT) + (uint32_t)r;
+        rd_o[pm] = ((((pm % NMAT) ? grid1 : grid0) + n * half_k) & 127u) >> 4;
+    }
     const uint32_t rd_row = (uint32_t)r * 128u, rd_sw = ((uint32_t)r >> 1) & 7u;
     unsigned char* ring = lds;
-    uint8_t* sl = lds + D * kRingSlot;
+    constexpr uint32_t kSlot = ring_slot<NP, NMAT>();
+    uint8_t* sl = lds + D * kSlot;
 
     f32x4 acc0[NP], acc1[NP];
 #pragma unroll
@@ -424,42 +442,46 @@ __device__ __forceinline__ void decode_pass_lds(const DArgs& a, const Tile tile,
     const uint32_t KG = K / 32, ns = (K + 255) / 256;
     u32x4 bq[2][2][4];  // activations of super-steps s and s+1 (two K steps each)
 
-    // issue order: scales, codes C_0 .. C_{D-2}, activations B_0; super-step s
-    // issues C_{s+D-1}, then B_{s+1}, after which B_s, C_s and all before them
-    // are all but the last 16 loads issued
+    // issue order: scales, line 0, line 1, activations B_0; super-step s
+    // issues line s + 2, then B_{s+1}, after which lines s, s + 1 and B_s
+    // are all but the last loads issued
     scales_dma<NP, NMAT>(s0, s1, c0, KG, sl, lane);
-#pragma unroll
-    for (int i = 0; i + 1 < D; ++i)
-        codes_dma<NP, NMAT>(w0, w1, lane_off, lane_ok, c0, K, (uint32_t)i, lane_k, ring + i * kRingSlot);
+    line_dma<NP, NMAT>(w0, w1, row_base, rel, half_k, 0, ring);
+    line_dma<NP, NMAT>(w0, w1, row_base, rel, half_k, 1, ring + kSlot);
     load_b<DT_MXFP4>(bsrc, b_base, has_row, K, 0, qd, bq[0][0]);
     load_b<DT_MXFP4>(bsrc, b_base, has_row, K, 1, qd, bq[0][1]);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
 
+    uint32_t slot_s = 0;  // ring slot of line s
     auto step = [&](uint32_t s, int cur) {
-        const uint32_t sn = s + (uint32_t)(D - 1);
-        codes_dma<NP, NMAT>(w0, w1, lane_off, lane_ok, c0, K, sn, lane_k, ring + (sn % D) * kRingSlot);
+        const uint32_t slot_s1 = slot_s == D - 1 ? 0 : slot_s + 1, slot_s2 = slot_s1 == D - 1 ? 0 : slot_s1 + 1;
+        line_dma<NP, NMAT>(w0, w1, row_base, rel, half_k, s + 2, ring + slot_s2 * kSlot);
         load_b<DT_MXFP4>(bsrc, b_base, has_row, K, 2 * (s + 1), qd, bq[cur ^ 1][0]);
         load_b<DT_MXFP4>(bsrc, b_base, has_row, K, 2 * (s + 1) + 1, qd, bq[cur ^ 1][1]);
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        // the last 2 NP NMAT + 8 loads issued: line s + 2 and B_{s+1}
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NP * NMAT + 8) : "memory");
         __builtin_amdgcn_sched_barrier(0);
-        const unsigned char* slot = ring + (s % D) * kRingSlot;
+        const unsigned char* line0 = ring + slot_s * kSlot + rd_row;
+        const unsigned char* line1 = ring + slot_s1 * kSlot + rd_row;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint32_t g = 2 * s + (uint32_t)h;  // past K: codes, scales and activations read as zeros
             Batch<MODE, DT_MXFP4, NP> x;
-            const uint32_t cpos = ((4u * (uint32_t)h + qd) ^ rd_sw) * 16u;
 #pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                x.wq[p] = *reinterpret_cast<const u32x4*>(slot + (p * NMAT) * 2048 + rd_row + cpos);
-                if constexpr (MODE == 0)
-                    x.uq[p] = *reinterpret_cast<const u32x4*>(slot + (p * NMAT + 1) * 2048 + rd_row + cpos);
+            for (int pm = 0; pm < NP * NMAT; ++pm) {
+                const uint32_t q = rd_o[pm] + 4u * (uint32_t)h + qd;  // unit from the start of line s
+                const unsigned char* src = (q & 8u) ? line1 : line0;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(src + pm * 2048 + (((q & 7u) ^ rd_sw) << 4));
+                if (pm % NMAT == 0) x.wq[pm / NMAT] = v;
+                else x.uq[pm / NMAT] = v;
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) x.b[j] = bq[cur][h][j];
             scales_fetch<MODE, DT_MXFP4, NP>(x, sl, nv, KG, g, r, qd);
             compute<MODE, DT_MXFP4, NP, true>(x, acc0, acc1);
         }
+        slot_s = slot_s1;
         asm volatile("" ::: "memory");
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -469,8 +491,8 @@ __device__ __forceinline__ void decode_pass_lds(const DArgs& a, const Tile tile,
         step(s, 0);
         step(s + 1, 1);
     }
-    // the copies still in flight read past K (zeros, no memory traffic) but
-    // write this wave's LDS: let them land before the wave ends
+    // the copies still in flight read past the rows (zeros, no memory traffic)
+    // but write this wave's LDS: let them land before the wave ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     store_block<MODE, NP>(a, acc0, acc1, perm, row0, r, qd, has_row, c0, c1);
 }
@@ -524,7 +546,7 @@ __global__ __launch_bounds__(kBlkWaves * 64) void decode_block_kernel(DArgs a) {
 
 // MXFP4, codes through LDS: one block per one-wave workgroup (the same split
 // of blocks); the LDS (D ring slots and the scales) caps the waves per CU.
-template <int MODE, int NP, int D>
+template <int MODE, int NP>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void decode_block_mxl_kernel(DArgs a) {
     const int lane = threadIdx.x & 63;
     const int ntl = min(a.n_tiles[0], a.max_tiles);
@@ -535,7 +557,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1))) void de
     if (mt >= ntl) return;
     const uint32_t c0 = (uint32_t)cb * kRows;
     extern __shared__ __align__(16) unsigned char dsm[];
-    decode_pass_lds<MODE, NP, D>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane, dsm);
+    decode_pass_lds<MODE, NP>(a, a.tiles[mt], a.perm_src, c0, min((uint32_t)a.N, c0 + kRows), lane, dsm);
 }
 
 // ------------------------------------------------ fused routing + gate/up --
@@ -862,7 +884,6 @@ int cu_count() {
 }
 
 constexpr int kMaxLds = 160 * 1024;
-constexpr int kMxRing = 2;  // MXFP4 decode: LDS ring slots (super-steps) for the codes
 
 template <auto Kern>
 hipError_t allow_lds() {
@@ -878,8 +899,9 @@ hipError_t launch_blocks(const GemmProblem& p, hipStream_t stream) {
         // LDS: the codes' ring, then the block's scales, [panel][matrix][16][K/32] bytes
         static_assert(kBlkWaves == 1, "one block per workgroup");
         if ((uint32_t)a.K / 32 > kScaleMaxKg) return hipErrorInvalidValue;  // beyond the MXFP4 K limit
-        const size_t smem = kMxRing * kRingSlot + (size_t)NP * (MODE == 0 ? 2 : 1) * scale_lines(a.K / 32) * 256;
-        decode_block_mxl_kernel<MODE, NP, kMxRing><<<blocks, 64, smem, stream>>>(a);
+        constexpr int NMAT = MODE == 0 ? 2 : 1;
+        const size_t smem = kMxRing * ring_slot<NP, NMAT>() + (size_t)NP * NMAT * scale_lines(a.K / 32) * 256;
+        decode_block_mxl_kernel<MODE, NP><<<blocks, 64, smem, stream>>>(a);
     } else {
         decode_block_kernel<MODE, WDT, DEPTH, NP><<<blocks, kBlkWaves * 64, 0, stream>>>(a);
     }
