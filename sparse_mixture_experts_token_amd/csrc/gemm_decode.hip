@@ -698,16 +698,25 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
     for (int i = tid; i < T * kFMaxE; i += kGuWaves * 64)
         if (i % kFMaxE >= E) skey[i] = 0ull;  // past E: below every key
     {
+        // an element past T*E reads element 0, and without a bias the bias
+        // reads are taken from the partial sums and dropped: no branch around
+        // the loads (a branch per element made the compiler wait for each
+        // group in turn)
         float pv[kFLogitsPerThread][kLogitSlices], bv[kFLogitsPerThread];
+        const bool has_br = f.br != nullptr;
+        const uint16_t* brp = has_br ? f.br : reinterpret_cast<const uint16_t*>(f.part);
 #pragma unroll
         for (int j = 0; j < kFLogitsPerThread; ++j) {
             const int i = tid + j * kGuWaves * 64;
             const bool in = i < T * E;
             const int t = in ? i / E : 0, e = in ? i - t * E : 0;
 #pragma unroll
-            for (int ks = 0; ks < kLogitSlices; ++ks) pv[j][ks] = in ? f.part[((size_t)ks * T + t) * E + e] : 0.f;
-            bv[j] = (in && f.br) ? bf16_bits_to_f32(f.br[e]) : 0.f;
+            for (int ks = 0; ks < kLogitSlices; ++ks) pv[j][ks] = f.part[((size_t)ks * T + t) * E + e];
+            bv[j] = bf16_bits_to_f32(brp[e]);
         }
+        __builtin_amdgcn_sched_barrier(0);  // every load above goes out before the first sum
+#pragma unroll
+        for (int j = 0; j < kFLogitsPerThread; ++j) bv[j] = has_br ? bv[j] : 0.f;
 #pragma unroll
         for (int j = 0; j < kFLogitsPerThread; ++j) {
             const int i = tid + j * kGuWaves * 64;
