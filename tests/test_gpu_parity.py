@@ -326,6 +326,34 @@ def _bf16_bits_of(x64: np.ndarray) -> np.ndarray:
     return (b >> 16).astype(np.uint16)
 
 
+@pytest.mark.parametrize("name", ["decode-mxfp4-staged-scales", "mxfp4-small"])
+def test_mxfp4_codes_off_the_line_grid(name):
+    """MXFP4 code blocks that start 16, 48 and 80 bytes past a 128-byte memory
+    line (views into larger buffers; the API asks for 16-byte alignment only).
+    The decode kernels copy codes along the memory's line grid, so these
+    starts take their line-offset arithmetic; the outputs must be bitwise
+    those of the same layer with line-aligned weights, and the layer must
+    still match the fp64 oracle."""
+    cfg = next(c for c in EDGE if c.name == name)
+    L = synth.make_layer(cfg)
+    st = L.stacked()
+    w = device_weights(L, st)
+    shifted = dict(w)
+    for n, off in (("w_gate", 48), ("w_up", 80), ("w_down", 16)):
+        t = w[n]
+        buf = torch.zeros(t.numel() + 256, dtype=torch.uint8, device=t.device)
+        v = buf[off:off + t.numel()].view(t.shape)
+        v.copy_(t)
+        assert v.data_ptr() % 128 == off
+        shifted[n] = v
+    prob = problem(cfg, L.T)
+    h = to_dev(L.h, cfg.act)
+    g0 = run(prob, w, h, cfg.act)
+    g1 = run(prob, shifted, h, cfg.act)
+    assert torch.equal(g0["out_raw"].view(torch.int16), g1["out_raw"].view(torch.int16))
+    check_layer(L, st, w_dev=shifted)
+
+
 def test_mxfp4_decode_bit_exact_every_code_and_scale():
     # every byte (two codes) with every scale 0..254: 16 groups of 16 bytes per scale
     packed = np.tile(np.arange(256, dtype=np.uint8).reshape(16, 16), (255, 1))
