@@ -350,13 +350,14 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
 // slower.  The block's 16 NP NMAT row lines (L = 16 (p NMAT + m) + r for
 // panel p, matrix m, row r of the panel) take 2 NP NMAT DMA instructions of
 // 16 bytes per lane, 8 lanes per line; a lane copies only the 16-byte units
-// inside its row (the rest read as zero, without memory traffic).  Smaller
-// blocks (16-row gate/up, 32-row down) measured slower.  Position u of line L in LDS
-// holds unit u ^ ((r >> 1) & 7) of the memory line: a K step reads 16 B at 16
-// rows of a panel with few bank conflicts.  A ring of three slots holds lines
-// s and s + 1 while line s + 2 is copied.  Step h (0, 1) of super-step s is K
-// step g = 2 s + h, with the K order of the register path (lane quarter qd
-// takes the codes of K [256 s + 32 c, + 32), c = 4 h + qd).
+// inside its row (the rest read as zero, without memory traffic).  Position
+// u of line L in LDS holds unit u ^ ((r >> 1) & 7) of the memory line: a K
+// step reads 16 B at 16 rows of a panel with few bank conflicts.  A ring of
+// three slots holds lines s and s + 1 while line s + 2 is copied.  Step h
+// (0, 1) of super-step s is K step g = 2 s + h, with the K order of the
+// register path (lane quarter qd takes the codes of K [256 s + 32 c, + 32),
+// c = 4 h + qd).  Smaller blocks (16-row gate/up, 32-row down) measured
+// slower.
 constexpr int kMxRing = 3;  // ring slots (lines) for the codes
 // bytes of one ring slot: a line of each of the block's 16 NP NMAT rows
 template <int NP, int NMAT>
@@ -466,7 +467,7 @@ __device__ __forceinline__ void decode_pass_lds(const DArgs& a, const Tile tile,
         const unsigned char* line1 = ring + slot_s1 * kSlot + rd_row;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t g = 2 * s + (uint32_t)h;  // past K: codes, scales and activations read as zeros
+            const uint32_t g = 2 * s + (uint32_t)h;  // past K: codes and activations read as zeros, the scale as one
             Batch<MODE, DT_MXFP4, NP> x;
 #pragma unroll
             for (int pm = 0; pm < NP * NMAT; ++pm) {
