@@ -121,7 +121,15 @@ __device__ __forceinline__ void bare_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g / (1 + e^-g) with the hardware reciprocal (about 1 ulp) in place
+// of the correctly rounded division, whose dozen instructions per element
+// made the epilogue a visible part of each work item; the product is rounded
+// to bf16 right after, 16 bits coarser.
+__device__ __forceinline__ float silu_fast(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+
+// A buffer offset beyond every range used by the stores below (ranges stay
+// under 2^30 bytes, so adding a row offset cannot wrap around).
+constexpr uint32_t kOobStore = 0x7ffffff0u;
 
 template <int MODE, int BN, int S, bool MXW>
 struct Cfg {
@@ -557,17 +565,31 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
     // ---- epilogue: D[v] of a 32x32 tile is row 8(v/4) + 4(l/32) + v%4, column l%32 ----
     const int fr = lane & 31, fh = lane >> 5;
     if constexpr (MODE == 0) {
+        // act = bf16(silu(g) u), stored as column pairs: lanes l and l^1 hold
+        // columns c and c+1 (c even) of the same rows, so one exchange per
+        // pair of rows v, v+1 gives the even lane row v and the odd lane row
+        // v+1 of both columns, one 4-byte store each.  The stores go through a
+        // buffer that spans the tile's rows of act: rows past the tile lie
+        // beyond it, columns past N get an offset beyond it, and the hardware
+        // drops both, so the loop has no branches.
+        const int odd = lane & 1;
+        const uint32_t N2 = (uint32_t)N * 2u;
+        const buf_rsrc ob =
+            make_rsrc(reinterpret_cast<const uint16_t*>(args.out) + (size_t)row0 * N, (uint32_t)rows * N2);
 #pragma unroll
-        for (int i = 0; i < C::MBW; ++i) {
+        for (int j = 0; j < C::NBW; ++j) {
+            const int n = n0 + (wn * C::NBW + j) * 32 + (fr & ~1);  // N is even: n < N covers n + 1
+            const uint32_t cb = n < N ? (uint32_t)(wm * 32 + 4 * fh + odd) * N2 + (uint32_t)n * 2u : kOobStore;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = (wm + kWM * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
-                if (r >= rows) continue;
-                uint16_t* orow = reinterpret_cast<uint16_t*>(args.out) + (size_t)(row0 + r) * N;
+            for (int i = 0; i < C::MBW; ++i) {
 #pragma unroll
-                for (int j = 0; j < C::NBW; ++j) {
-                    const int n = n0 + (wn * C::NBW + j) * 32 + fr;
-                    if (n < N) orow[n] = (uint16_t)f32_to_bf16_bits(silu_f(acc[0][i][j][v]) * acc[1][i][j][v]);
+                for (int v = 0; v < 16; v += 2) {
+                    const float a0 = silu_fast(acc[0][i][j][v]) * acc[1][i][j][v];
+                    const float a1 = silu_fast(acc[0][i][j][v + 1]) * acc[1][i][j][v + 1];
+                    const float got = dpp_f<kDppXor1>(odd ? a0 : a1);
+                    const uint32_t w = pack_bf16x2(odd ? got : a0, odd ? a1 : got);
+                    const uint32_t ro = (uint32_t)(kWM * i * 32 + 8 * (v >> 2) + (v & 3)) * N2;
+                    __builtin_amdgcn_raw_buffer_store_b32(w, ob, cb + ro, 0, 0);
                 }
             }
         }
@@ -585,6 +607,11 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
         }
         wait_lds_reads();
         bare_barrier();
+        // One address per row: the NBW stores of a row are 128 bytes apart
+        // (immediate offsets), and a tile that lies wholly inside N (every
+        // tile when BN divides N) needs no column test.
+        const int nb = n0 + wn * C::NBW * 32 + fr;  // this lane's first column
+        const bool full = n0 + BN <= N;             // the same for the whole workgroup
 #pragma unroll
         for (int i = 0; i < C::MBW; ++i) {
             int2 ap[16];
@@ -598,11 +625,14 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
                 const int r = (wm + kWM * i) * 32 + 8 * (v >> 2) + 4 * fh + (v & 3);
                 if (r >= rows) continue;
                 const float p = __int_as_float(ap[v].y);
-                float* orow = reinterpret_cast<float*>(args.out) + (size_t)ap[v].x * N;
+                float* orow = reinterpret_cast<float*>(args.out) + (size_t)ap[v].x * N + nb;
+                if (full) {
 #pragma unroll
-                for (int j = 0; j < C::NBW; ++j) {
-                    const int n = n0 + (wn * C::NBW + j) * 32 + fr;
-                    if (n < N) orow[n] = acc[0][i][j][v] * p;
+                    for (int j = 0; j < C::NBW; ++j) orow[j * 32] = acc[0][i][j][v] * p;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < C::NBW; ++j)
+                        if (nb + j * 32 < N) orow[j * 32] = acc[0][i][j][v] * p;
                 }
             }
         }
@@ -739,6 +769,7 @@ hipError_t launch_mode(size_t smem, const BArgs& a, hipStream_t stream) {
 
 hipError_t launch_gateup_bf16w(const GemmProblem& p, hipStream_t stream) {
     const BArgs a = make_args(p, 0);
+    if ((size_t)kBM * (size_t)a.N * 2u >= ((size_t)1 << 30)) return hipErrorInvalidValue;  // epilogue buffer range
     if (p.expert_dtype == DT_MXFP4) return launch_mode<gateup_bf16_kernel<true>>(CfgGateUp<true>::smem(a.K), a, stream);
     return launch_mode<gateup_bf16_kernel<false>>(CfgGateUp<false>::smem(a.K), a, stream);
 }

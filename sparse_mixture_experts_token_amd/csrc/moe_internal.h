@@ -55,6 +55,15 @@ __device__ __forceinline__ uint32_t buf_load1(buf_rsrc r, uint32_t voff, uint32_
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
+// Two floats to a bf16 pair (lo in the low half), round to nearest, ties to
+// even, by the hardware conversion (NaN stays NaN).
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_hw v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw));
+}
+
 // Round to nearest, ties to even (NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
     uint32_t u = __float_as_uint(f);
