@@ -49,13 +49,34 @@ def oracle_weights(layer: synth.Layer, stacked: dict) -> oracle.LayerWeights:
                                             lambda e: {n: a[e] for n, a in stacked.items()})
 
 
+GUARD = 4096     # canary bytes before and after every buffer the library writes
+CANARY = 0xA5
+_guarded: list = []
+
+
 def poisoned(shape, dtype, byte: int = 0xFF, device="cuda") -> torch.Tensor:
     """A tensor whose every byte is ``byte``: 0xFF reads as NaN in fp32 and
     bf16 and as -1 in int32, so a result the library fails to write, or a
-    workspace region it reads before writing, shows up in the comparison."""
-    t = torch.empty(shape, dtype=dtype, device=device)
-    t.view(torch.uint8).fill_(byte)
-    return t
+    workspace region it reads before writing, shows up in the comparison.
+    The tensor sits between two GUARD-byte runs of CANARY (its start stays
+    16-byte aligned); ``check_canaries`` then shows any write just outside it."""
+    n = int(np.prod(shape, dtype=np.int64)) * torch.empty((), dtype=dtype).element_size()
+    raw = torch.empty(n + 2 * GUARD, dtype=torch.uint8, device=device)
+    raw.fill_(CANARY)
+    raw[GUARD:GUARD + n].fill_(byte)
+    _guarded.append((raw, n))
+    return raw[GUARD:GUARD + n].view(dtype).view(shape)
+
+
+def check_canaries() -> None:
+    """Every buffer made by ``poisoned`` since the last check still has its
+    canary runs intact (call after the stream has been synchronized)."""
+    try:
+        for raw, n in _guarded:
+            assert bool((raw[:GUARD] == CANARY).all()), "write before the start of a buffer"
+            assert bool((raw[GUARD + n:] == CANARY).all()), "write past the end of a buffer"
+    finally:
+        _guarded.clear()
 
 
 def routing_outputs(T: int, E: int, k: int, dev, byte: int = 0xFF) -> dict:
@@ -69,7 +90,8 @@ def routing_outputs(T: int, E: int, k: int, dev, byte: int = 0xFF) -> dict:
 def run(prob: smoe.Problem, w: dict, h: torch.Tensor, act_fmt: str, byte: int = 0xFF) -> dict:
     """One forward pass with every routing output requested; results as numpy.
     The workspace, the output and the routing outputs are filled with
-    ``byte`` first (0xFF: NaN), so stale or unwritten data cannot pass."""
+    ``byte`` first (0xFF: NaN), so stale or unwritten data cannot pass, and
+    each is fenced by canary bytes that must survive the call."""
     T, E, k, H = prob.T, prob.E, prob.k, prob.H
     dev = h.device
     out = poisoned((T, H), h.dtype, byte, dev)
@@ -78,6 +100,7 @@ def run(prob: smoe.Problem, w: dict, h: torch.Tensor, act_fmt: str, byte: int = 
     ws = poisoned((max(nb, 1),), torch.uint8, byte, dev)
     smoe.moe_forward(prob, w, h, out, routing=r, workspace=ws, workspace_bytes=nb)
     torch.cuda.synchronize()
+    check_canaries()
     res = {n: t.cpu().numpy() for n, t in r.items()}
     res["out"] = out.float().cpu().numpy().astype(np.float64)
     res["out_raw"] = out.cpu()

@@ -14,8 +14,8 @@ import torch
 import oracle
 import sparse_mixture_experts_token_amd as smoe
 import synth
-from gpu_util import (check_out, device_weights, oracle_weights, poisoned, problem, reconcile, routing_outputs, to_dev,
-                      workers)
+from gpu_util import (check_canaries, check_out, device_weights, oracle_weights, poisoned, problem, reconcile,
+                      routing_outputs, to_dev, workers)
 
 pytestmark = pytest.mark.gpu
 
@@ -23,7 +23,8 @@ EPS = 1e-5
 
 
 def run_block(prob, w, g, x, eps=EPS, byte=0xFF):
-    """Workspace, output and routing outputs filled with ``byte`` (0xFF: NaN) first."""
+    """Workspace, output and routing outputs filled with ``byte`` (0xFF: NaN)
+    first, each fenced by canary bytes that must survive the call."""
     T, E, k, H = prob.T, prob.E, prob.k, prob.H
     dev = x.device
     out = poisoned((T, H), x.dtype, byte, dev)
@@ -32,6 +33,7 @@ def run_block(prob, w, g, x, eps=EPS, byte=0xFF):
     ws = poisoned((max(nb, 1),), torch.uint8, byte, dev)
     smoe.moe_block_forward(prob, w, g, eps, x, out, routing=r, workspace=ws, workspace_bytes=nb)
     torch.cuda.synchronize()
+    check_canaries()
     res = {n: t.cpu().numpy() for n, t in r.items()}
     res["out"] = out.float().cpu().numpy().astype(np.float64)
     res["out_raw"] = out.cpu()

@@ -10,7 +10,7 @@ import torch
 
 import sparse_mixture_experts_token_amd as smoe
 import synth
-from gpu_util import device_weights, poisoned, problem, routing_outputs, run, to_dev
+from gpu_util import check_canaries, device_weights, poisoned, problem, routing_outputs, run, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +21,7 @@ def _noalloc(prob, w, h):
     r = routing_outputs(T, E, k, h.device)
     smoe.moe_forward_noalloc(prob, w, h, out, routing=r)
     torch.cuda.synchronize()
+    check_canaries()
     res = {n: t.cpu().numpy() for n, t in r.items()}
     res["out_raw"] = out.cpu()
     return res
