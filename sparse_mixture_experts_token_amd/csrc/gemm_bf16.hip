@@ -81,6 +81,7 @@ struct BArgs {
     const uint8_t* s1;
     const int32_t* perm_src;
     const float* topk_w;
+    const float* row_p;     // routing weight of each expert-major row (down)
     const Tile* tiles;
     const int32_t* work;    // row tile * n_ntiles + column tile, expert-grouped order
     const int32_t* n_work;
@@ -595,15 +596,17 @@ __device__ __forceinline__ void process_item(const BArgs& args, int q) {
         }
     } else {
         // Each row's assignment and routing weight, fetched once per tile (two
-        // dependent loads per row) into the LDS ring, idle once every wave has
-        // read its last fragments; the stores below then wait on no load.  The
-        // next item's DMA into the ring follows the barrier of the work loop.
+        // independent loads per row: the weight is stored per row beside the
+        // permutation) into the LDS ring, idle once every wave has read its
+        // last fragments; the stores below then wait on no load.  The next
+        // item's DMA into the ring follows the barrier of the work loop.
         int2* rtab = reinterpret_cast<int2*>(smem);
         wait_lds_reads();
         bare_barrier();
         if (tid < rows) {  // rows <= kBM <= kThreads
             const int asg = args.perm_src[row0 + tid];
-            rtab[tid] = make_int2(asg, __float_as_int(args.topk_w[asg]));
+            const float pw = args.row_p[row0 + tid];
+            rtab[tid] = make_int2(asg, __float_as_int(pw));
         }
         wait_lds_reads();
         bare_barrier();
@@ -684,6 +687,7 @@ BArgs make_args(const GemmProblem& p, int mode) {
     BArgs a{};
     a.perm_src = p.perm_src;
     a.topk_w = p.topk_w;
+    a.row_p = p.row_p;
     a.tiles = p.tiles;
     a.k = p.k;
     if (mode == 0) {

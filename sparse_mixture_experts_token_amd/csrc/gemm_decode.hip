@@ -70,6 +70,7 @@ struct DArgs {
     const uint8_t* s1;
     const int32_t* perm_src;
     const float* topk_w;
+    const float* row_p;  // routing weight of each expert-major row (down)
     const Tile* tiles;
     const int32_t* n_tiles;
     void* out;          // act [T*k][N] bf16 (gate/up) or Y [T*k][N] f32 (down)
@@ -238,8 +239,8 @@ __device__ __forceinline__ void scales_fetch(Batch<MODE, WDT, NP>& x, const uint
 // those four rows are all present or all absent.
 template <int MODE, int NP>
 __device__ __forceinline__ void store_block(const DArgs& a, const f32x4 (&acc0)[NP], const f32x4 (&acc1)[NP],
-                                            const int32_t* perm, int row0, int r, uint32_t qd, bool has_row,
-                                            uint32_t c0, uint32_t c1) {
+                                            int row0, int r, uint32_t qd, bool has_row, uint32_t c0, uint32_t c1,
+                                            int asg, float pw) {
     const uint32_t N = (uint32_t)a.N;
     if (!has_row) return;
     if constexpr (MODE == 0) {
@@ -254,8 +255,6 @@ __device__ __forceinline__ void store_block(const DArgs& a, const f32x4 (&acc0)[
             *reinterpret_cast<uint2*>(orow + n0) = uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
         }
     } else {
-        const int asg = perm[row0 + r];
-        const float pw = a.topk_w[asg];
         float* orow = reinterpret_cast<float*>(a.out) + (size_t)asg * N;
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
@@ -337,7 +336,15 @@ __device__ __forceinline__ void decode_pass(const DArgs& a, const Tile tile, con
         }
     }
 
-    store_block<MODE, NP>(a, acc0, acc1, perm, row0, r, qd, has_row, c0, c1);
+    // down: the row's assignment and routing weight, two independent loads
+    // (loading them before the K loop measured slower here)
+    int asg = 0;
+    float pw = 0.f;
+    if (MODE == 1 && has_row) {
+        asg = perm[row0 + r];
+        pw = a.row_p[row0 + r];
+    }
+    store_block<MODE, NP>(a, acc0, acc1, row0, r, qd, has_row, c0, c1, asg, pw);
 }
 
 // MXFP4 codes through LDS.  A super-step is 256 K: 128 bytes of every weight
@@ -388,9 +395,15 @@ __device__ __forceinline__ void decode_pass_lds(const DArgs& a, const Tile tile,
 
     const bool has_row = r < rows;
     uint32_t b_base = 0;
+    int asg = 0;     // down: this lane's row's assignment and routing weight, loaded
+    float pw = 0.f;  // now (two independent loads) for the stores at the end
     if (has_row) {
         const int src = MODE == 0 ? perm[row0 + r] / a.k : row0 + r;
         b_base = (uint32_t)src * K * 2u;
+        if constexpr (MODE == 1) {
+            asg = perm[row0 + r];
+            pw = a.row_p[row0 + r];
+        }
     }
     const buf_rsrc bsrc = make_rsrc(a.a_src, a.a_bytes);
     bool nv[NP];
@@ -495,7 +508,7 @@ __device__ __forceinline__ void decode_pass_lds(const DArgs& a, const Tile tile,
     // the copies still in flight read past the rows (zeros, no memory traffic)
     // but write this wave's LDS: let them land before the wave ends
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    store_block<MODE, NP>(a, acc0, acc1, perm, row0, r, qd, has_row, c0, c1);
+    store_block<MODE, NP>(a, acc0, acc1, row0, r, qd, has_row, c0, c1, asg, pw);
 }
 
 // This wave's equal share of the (tile, weight row) pairs, tile-major, in
@@ -650,13 +663,14 @@ struct FArgs {
     int32_t* offsets;   // [E+1]
     int32_t* perm_src;  // [T*k]
     int32_t* inv;       // [T*k]
+    float* row_p;       // [T*k]
     Tile* tiles;        // [max_tiles]
     int32_t* n_tiles;   // [1]
 };
 
 // LDS layout of the fused kernel (byte offsets), identical on host and device.
 struct FLayout {
-    uint32_t sl, key, mask, off, toff, ti, perm, tiles, total;
+    uint32_t sl, key, mask, off, toff, ti, tw, perm, tiles, total;
 };
 __host__ __device__ inline uint32_t align16(uint32_t x) { return (x + 15u) & ~15u; }
 __host__ __device__ inline FLayout flayout(int T, int k, int max_tiles) {
@@ -668,6 +682,7 @@ __host__ __device__ inline FLayout flayout(int T, int k, int max_tiles) {
     L.off = o;   o += align16((kFMaxE + 1) * 4);
     L.toff = o;  o += align16((kFMaxE + 1) * 4);
     L.ti = o;    o += align16((uint32_t)T * k * 4);       // selected expert of each assignment
+    L.tw = o;    o += align16((uint32_t)T * k * 4);       // its routing weight
     L.perm = o;  o += align16((uint32_t)T * k * 4);       // assignment of each expert-major row
     L.tiles = o; o += align16((uint32_t)max_tiles * sizeof(Tile));
     L.total = o;
@@ -686,6 +701,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
     int32_t* off = reinterpret_cast<int32_t*>(smem + L.off);
     int32_t* toff = reinterpret_cast<int32_t*>(smem + L.toff);
     int32_t* ti = reinterpret_cast<int32_t*>(smem + L.ti);
+    float* tw = reinterpret_cast<float*>(smem + L.tw);
     int32_t* perm = reinterpret_cast<int32_t*>(smem + L.perm);
     Tile* tl = reinterpret_cast<Tile*>(smem + L.tiles);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -766,6 +782,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
             const int pos = __popc(balh & lt);  // ascending expert order
             if (chosen) {
                 ti[t * k + pos] = le;
+                tw[t * k + pos] = z / zs;
                 atomicOr(&emask[le], 1ull << t);
                 if (writer) {
                     f.topk_idx[(size_t)t * k + pos] = le;
@@ -789,6 +806,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
             const int pos = __popcll(bal & lt);  // ascending expert order
             if (chosen) {
                 ti[t * k + pos] = lane;
+                tw[t * k + pos] = z / zs;
                 atomicOr(&emask[lane], 1ull << t);
                 if (writer) {
                     f.topk_idx[(size_t)t * k + pos] = lane;
@@ -844,6 +862,7 @@ __global__ __launch_bounds__(kGuWaves * 64) void decode_route_gateup_kernel(FArg
         if (writer) {
             f.perm_src[row] = as;
             f.inv[as] = row;
+            f.row_p[row] = tw[as];
         }
     }
     __syncthreads();
@@ -856,6 +875,7 @@ DArgs make_dargs(const GemmProblem& p, int mode) {
     DArgs a{};
     a.perm_src = p.perm_src;
     a.topk_w = p.topk_w;
+    a.row_p = p.row_p;
     a.tiles = p.tiles;
     a.n_tiles = p.n_tiles;
     a.k = p.k;
@@ -956,6 +976,7 @@ hipError_t launch_fused(const GemmProblem& p, const FusedRouting& r, hipStream_t
     f.offsets = r.offsets;
     f.perm_src = r.perm_src;
     f.inv = r.inv;
+    f.row_p = r.row_p;
     f.tiles = r.tiles;
     f.n_tiles = r.n_tiles;
     const FLayout L = flayout(p.T, p.k, p.max_tiles);

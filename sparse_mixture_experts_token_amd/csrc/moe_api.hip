@@ -67,7 +67,7 @@ int check_problem(const moe_problem* p) {
 
 // Workspace regions, in order.
 struct Layout {
-    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, tiles, ntiles, queues, work0, work1, part, act, y,
+    size_t topk_idx, topk_w, blk, rank, offsets, perm, inv, rowp, tiles, ntiles, queues, work0, work1, part, act, y,
         total;
     int nblk, max_tiles, BM, nc0, nc1;
     bool decode;
@@ -97,6 +97,7 @@ Layout layout(const moe_problem* p, int router_dt = -1, bool all_plogits = false
     L.offsets = o;  o = align_up(o + ((size_t)p->E + 1) * 4);
     L.perm = o;     o = align_up(o + tk * 4);
     L.inv = o;      o = align_up(o + tk * 4);
+    L.rowp = o;     o = align_up(o + tk * 4);
     L.tiles = o;    o = align_up(o + (size_t)L.max_tiles * sizeof(Tile));
     L.ntiles = o;   o = align_up(o + 256);  // tile count, the two work-list counts, then at ints 16 and 32
                                             // the two lists' XCD range bounds
@@ -251,6 +252,7 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     int32_t* blk = (int32_t*)(ws + L.blk);
     int32_t* rank = (int32_t*)(ws + L.rank);
     int32_t* inv = (int32_t*)(ws + L.inv);
+    float* row_p = (float*)(ws + L.rowp);
     Tile* tiles = (Tile*)(ws + L.tiles);
     int32_t* ntiles = (int32_t*)(ws + L.ntiles);
     void* act = ws + L.act;
@@ -285,8 +287,8 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     }
     mark(1);
     if (!L.fused) {
-        e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, tiles, ntiles,
-                                   L.max_tiles, wl0, wl1, queues, moe::kNumQueues, stream);
+        e = moe::launch_route_scan(p->T, p->E, p->k, L.BM, topk_idx, blk, rank, offsets, perm, inv, topk_w, row_p,
+                                   tiles, ntiles, L.max_tiles, wl0, wl1, queues, moe::kNumQueues, stream);
         if (e != hipSuccess) return MOE_ERR_HIP;
     }
     mark(2);
@@ -300,6 +302,7 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     g.s_gate = w->s_gate; g.s_up = w->s_up; g.s_down = w->s_down;
     g.perm_src = perm;
     g.topk_w = topk_w;
+    g.row_p = row_p;
     g.tiles = tiles;
     g.n_tiles = ntiles;
     g.max_tiles = L.max_tiles;
@@ -314,7 +317,7 @@ int run_pass(const moe_problem* p, const moe_weights* w, const PassIn& in, void*
     g.decode = L.decode;
     g.queues = queues;
     if (L.fused) {
-        const moe::FusedRouting fr{part, in.b_router, logits, topk_idx, topk_w, offsets, perm, inv, tiles, ntiles};
+        const moe::FusedRouting fr{part, in.b_router, logits, topk_idx, topk_w, offsets, perm, inv, row_p, tiles, ntiles};
         e = moe::launch_route_gateup_decode(g, fr, stream);
     } else {
         e = moe::launch_gateup(g, stream);

@@ -255,7 +255,8 @@ constexpr int kItemFixedCost[2] = {5, 5};
 hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx,
                              int32_t* blk_counts /*in: counts, out: bases*/,
                              const int32_t* local_rank, int32_t* offsets /*[E+1]*/,
-                             int32_t* perm_src, int32_t* inv, Tile* tiles, int32_t* n_tiles,
+                             int32_t* perm_src, int32_t* inv, const float* topk_w, float* row_p,
+                             Tile* tiles, int32_t* n_tiles,
                              int max_tiles, WorkList w0, WorkList w1, int32_t* zero, int n_zero,
                              hipStream_t stream);
 
@@ -272,6 +273,7 @@ struct GemmProblem {
     const uint8_t* s_down;
     const int32_t* perm_src;
     const float* topk_w;
+    const float* row_p;  // [T*k] topk_w[perm_src[r]] per expert-major row r (written with perm_src)
     const Tile* tiles;
     const int32_t* n_tiles;
     int max_tiles;
@@ -313,6 +315,7 @@ struct FusedRouting {
     int32_t* offsets;
     int32_t* perm_src;
     int32_t* inv;
+    float* row_p;
     Tile* tiles;
     int32_t* n_tiles;
 };

@@ -7,6 +7,8 @@
 //               ordered by token (a stable counting sort: no atomics, so the
 //               result is unique and run-to-run identical)
 //   inv[a]      the row of assignment a
+//   row_p[r]    topk_w[perm_src[r]], the routing weight of row r (so that the
+//               down product's epilogue needs no dependent load)
 //   tiles       the (expert, first row, rows) tiles of at most BM rows that the
 //               grouped GEMMs walk; experts without tokens get no tile.
 //   work lists  the order in which the GEMM workgroups take (row tile, column
@@ -40,7 +42,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
                                                           int32_t* __restrict__ blk,  // [E][nblk]
                                                           const int32_t* __restrict__ local_rank,
                                                           int32_t* __restrict__ offsets, int32_t* __restrict__ perm_src,
-                                                          int32_t* __restrict__ inv, Tile* __restrict__ tiles,
+                                                          int32_t* __restrict__ inv, const float* __restrict__ topk_w,
+                                                          float* __restrict__ row_p, Tile* __restrict__ tiles,
                                                           int32_t* __restrict__ n_tiles, int max_tiles, WorkList w0,
                                                           WorkList w1, int32_t* __restrict__ zero, int n_zero,
                                                           bool scatter_outside) {
@@ -247,11 +250,13 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
     const int total = T * k;
     for (int a0 = 0; a0 < total; a0 += 1024 * kScatterPer) {
         int e[kScatterPer], lr[kScatterPer];
+        float tw[kScatterPer];
 #pragma unroll
         for (int j = 0; j < kScatterPer; ++j) {
             const int a = a0 + j * 1024 + tid;
             e[j] = a < total ? topk_idx[a] : 0;
             lr[j] = a < total ? local_rank[a] : 0;
+            tw[j] = a < total ? topk_w[a] : 0.f;
         }
 #pragma unroll
         for (int j = 0; j < kScatterPer; ++j) {
@@ -262,6 +267,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int T, int E, int k, i
                 const int r = offs[e[j]] + (in_lds ? base_lds[bi] : blk[bi]) + lr[j];
                 perm_src[r] = a;
                 inv[a] = r;
+                row_p[r] = tw[j];
             }
         }
     }
@@ -274,7 +280,9 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(int total, int k, in
                                                             const int32_t* __restrict__ bases,
                                                             const int32_t* __restrict__ local_rank,
                                                             const int32_t* __restrict__ offsets,
-                                                            int32_t* __restrict__ perm_src, int32_t* __restrict__ inv) {
+                                                            int32_t* __restrict__ perm_src, int32_t* __restrict__ inv,
+                                                            const float* __restrict__ topk_w,
+                                                            float* __restrict__ row_p) {
     const int a = blockIdx.x * 256 + threadIdx.x;
     if (a >= total) return;
     const int e = topk_idx[a];
@@ -282,6 +290,7 @@ __global__ __launch_bounds__(256) void route_scatter_kernel(int total, int k, in
     const int r = offsets[e] + bases[(size_t)e * nblk + b] + local_rank[a];
     perm_src[r] = a;
     inv[a] = r;
+    row_p[r] = topk_w[a];
 }
 
 // Batches of more assignments than this scatter in their own launch.
@@ -291,16 +300,18 @@ constexpr int kScatterInKernelMax = 4096;
 
 hipError_t launch_route_scan(int T, int E, int k, int BM, const int32_t* topk_idx, int32_t* blk_counts,
                              const int32_t* local_rank, int32_t* offsets, int32_t* perm_src, int32_t* inv,
-                             Tile* tiles, int32_t* n_tiles, int max_tiles, WorkList w0, WorkList w1, int32_t* zero,
-                             int n_zero, hipStream_t stream) {
+                             const float* topk_w, float* row_p, Tile* tiles, int32_t* n_tiles, int max_tiles,
+                             WorkList w0, WorkList w1, int32_t* zero, int n_zero, hipStream_t stream) {
     const int total = T * k;
     const bool outside = total > kScatterInKernelMax;
     route_scan_kernel<<<1, 1024, 0, stream>>>(T, E, k, BM, topk_idx, blk_counts, local_rank, offsets, perm_src, inv,
-                                              tiles, n_tiles, max_tiles, w0, w1, zero, n_zero, outside);
+                                              topk_w, row_p, tiles, n_tiles, max_tiles, w0, w1, zero, n_zero,
+                                              outside);
     if (outside) {
         const int nblk = (T + kRouterTokens - 1) / kRouterTokens;
         route_scatter_kernel<<<(total + 255) / 256, 256, 0, stream>>>(total, k, nblk, topk_idx, blk_counts,
-                                                                      local_rank, offsets, perm_src, inv);
+                                                                      local_rank, offsets, perm_src, inv, topk_w,
+                                                                      row_p);
     }
     return hipGetLastError();
 }
